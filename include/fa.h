@@ -1,0 +1,97 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) FlashAttention forward library (libfa_fwd.so).
+ *
+ * The operation is exact scaled dot-product attention with one log-sum-exp per
+ * query row, computed tile by tile with the online-softmax recurrence so that no
+ * M x N score or probability matrix exists in memory:
+ *
+ *   S = scale * Q K^T,   P = row-softmax(S),   O = P V,   LSE_i = m_i + ln(sum_j exp(S_ij - m_i))
+ *
+ * Definition: "Module 08: FlashAttention and Memory-Efficient Kernels"
+ * (backend-roadmap), sections "Where the time goes in standard attention",
+ * "Tiling and the online softmax" and "The backward pass: recompute instead of
+ * store" (the per-row L = m + log(l)); problem statement and shapes (Q is M x D,
+ * K and V are N x D, O is M x D): "FlashAttention in Triton: A Tile-by-Tile
+ * Walkthrough", section "First, what does attention actually do?"; the caller
+ * pre-allocates the output the kernel writes into, as that page's launcher does.
+ *
+ * Causal masking is aligned to the bottom-right corner: key j is visible to
+ * query i iff j <= i + (N - M) (the pages' lower-triangular mask when M == N).
+ * A query row with no visible key (causal with M > N, or N == 0) gets O = 0 and
+ * LSE = -inf.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o.  lse is always fp32. */
+typedef enum {
+  FA_DTYPE_F32 = 0,  /* IEEE fp32 in and out; P stays fp32 for the PV product   */
+  FA_DTYPE_F16 = 1,  /* IEEE half; fp32 accumulation, P rounded to half for PV  */
+  FA_DTYPE_BF16 = 2  /* bfloat16; fp32 accumulation, P rounded to bf16 for PV   */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,       /* a required pointer is NULL                               */
+  FA_ERR_BAD_SHAPE = 2,      /* B, H, M or N negative                                    */
+  FA_ERR_BAD_DTYPE = 3,      /* dtype is not one of fa_dtype_t                            */
+  FA_ERR_UNSUPPORTED_D = 4,  /* D outside 1..128                                          */
+  FA_ERR_BAD_SCALE = 5,      /* scale not finite or not > 0                               */
+  FA_ERR_MISALIGNED = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte       */
+  FA_ERR_TOO_LARGE = 7,      /* a per-head extent or the grid exceeds the 32-bit limits   */
+  FA_ERR_HIP = 8             /* the HIP runtime reported an error at launch               */
+} fa_status_t;
+
+/*
+ * fa_fwd - enqueue the attention forward pass on `stream`.
+ *
+ * Arguments (all pointers are DEVICE pointers owned by the caller; the library
+ * allocates nothing, keeps no per-call state and never synchronises):
+ *   q    [B, H, M, D]  contiguous row-major, element type `dtype`
+ *   k    [B, H, N, D]  contiguous row-major, element type `dtype`
+ *   v    [B, H, N, D]  contiguous row-major, element type `dtype`
+ *   o    [B, H, M, D]  contiguous row-major, element type `dtype` (written)
+ *   lse  [B, H, M]     contiguous fp32, natural-log units (written)
+ *   scale              the multiplier of Q K^T (typically 1/sqrt(D)); finite, > 0
+ *   causal             0: every key visible; 1: bottom-right causal mask
+ *   dtype              an fa_dtype_t value
+ *   stream             a hipStream_t, or NULL for the default stream
+ * o and lse must not overlap q, k or v.  Output rounding to f16/bf16 is
+ * round-to-nearest-even.
+ *
+ * Returns FA_OK once the work is enqueued.  Every argument error is detected on
+ * the host before any HIP call; then nothing is launched and o and lse are not
+ * touched.  Empty problems (B, H or M zero) return FA_OK without a launch, and
+ * pointers may then be NULL.  N == 0 is valid (k and v may be NULL): every row
+ * is empty.  A device-side fault shows at the caller's next synchronisation.
+ * Limits: 1 <= D <= 128; M*D and N*D below 2^31; B*H*ceil(M/128) below 2^31.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+           float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_check_args - the host-side validation fa_fwd performs, with the same
+ * arguments and return codes, and no HIP call (usable without a GPU).
+ */
+int fa_check_args(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                  int64_t D, float scale, int causal, int dtype);
+
+/* fa_status_string - a static, human-readable name for a status code. */
+const char* fa_status_string(int status);
+
+/* fa_abi_version - the ABI revision of this header (currently 1). */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,132 @@
+"""Python binding of libfa_fwd.so, the gfx950 FlashAttention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/fa.h``.  PyTorch is used for
+device memory and the current HIP stream, nothing else.  There is no fallback:
+if the library is missing or fails to load, every call raises.
+
+Functions with the C names take raw integers (device addresses, sizes) exactly
+as the C ABI does; :func:`fwd` is the tensor-level convenience wrapper.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_check_args", "fa_status_string",
+           "fa_abi_version", "fwd", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "STATUS"]
+
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_BAD_DTYPE",
+    4: "FA_ERR_UNSUPPORTED_D", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_MISALIGNED",
+    7: "FA_ERR_TOO_LARGE", 8: "FA_ERR_HIP",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str = "fa_fwd"):
+        self.status = status
+        super().__init__(f"{where} failed: {fa_status_string(status)} ({status})")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfa_fwd.so")
+
+
+def load():
+    """Load libfa_fwd.so (once) and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m io_aware_tiled_fa_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    i64, vp, fp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp, ctypes.c_int,
+                           ctypes.c_int, vp]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp,
+                                  ctypes.c_int, ctypes.c_int]
+    lib.fa_check_args.restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream=None) -> int:
+    """Direct call of the C entry point; pointers are integer device addresses."""
+    return load().fa_fwd(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal), int(dtype),
+                         stream)
+
+
+def fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype) -> int:
+    return load().fa_check_args(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal),
+                                int(dtype))
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_abi_version() -> int:
+    return load().fa_abi_version()
+
+
+def _dtype_code(t):
+    import torch
+
+    codes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
+        stream=None):
+    """O, LSE = attention forward of q [B,H,M,D], k/v [B,H,N,D] (device tensors).
+
+    Allocates ``o`` (like q) and ``lse`` ([B,H,M] fp32) unless given, enqueues
+    fa_fwd on ``stream`` (default: torch's current stream) and returns them.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, seq, D]")
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    if tuple(k.shape) != (B, H, N, D) or tuple(v.shape) != (B, H, N, D):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise ValueError("q, k, v must be device tensors")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, M, N, D, scale, 1 if causal else 0, code, stream)
+    if st != 0:
+        raise FaError(st)
+    return out, lse

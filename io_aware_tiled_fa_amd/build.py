@@ -1,0 +1,64 @@
+"""Build libfa_fwd.so in-tree: the gfx950 HIP kernels plus the host-only validation unit.
+
+    python -m io_aware_tiled_fa_amd.build
+
+Object files go to ``_build/`` at the repository root; the shared library is
+written next to this file, where the binding loads it from.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libfa_fwd.so")
+
+ARCH = "gfx950"
+# Every HIP translation unit is built without packed-fp32 VALU instructions.
+HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}"]
+C_FLAGS = ["-O2", "-fPIC", "-std=c11", "-Wall", "-Wextra", f"-I{INCLUDE}"]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libfa_fwd.so")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler (gcc) found")
+    check_o = os.path.join(BUILD, "fa_check.o")
+    fwd_o = os.path.join(BUILD, "fa_fwd.o")
+    _run([cc, *C_FLAGS, "-c", os.path.join(CSRC, "fa_check.c"), "-o", check_o], verbose)
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_fwd.hip"), "-o", fwd_o], verbose)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, fwd_o, check_o], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,57 @@
+/*
+ * fa_check.c - host-side argument validation of fa_fwd (no HIP dependency).
+ *
+ * Compiled with the host C compiler so that it can be unit-tested and run
+ * under a host sanitizer without a GPU.  fa_fwd calls fa_check_args first and
+ * launches nothing unless it returns FA_OK.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+#define FA_BLOCK_M 128 /* query rows per workgroup (must match the kernels) */
+
+static int aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int fa_check_args(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                  int64_t D, float scale, int causal, int dtype) {
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return FA_ERR_BAD_DTYPE;
+  if (B < 0 || H < 0 || M < 0 || N < 0) return FA_ERR_BAD_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_BAD_SHAPE;
+  if (D < 1 || D > 128) return FA_ERR_UNSUPPORTED_D;
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_BAD_SCALE;
+  if (B == 0 || H == 0 || M == 0) return FA_OK; /* nothing to compute */
+  if (q == NULL || o == NULL || lse == NULL) return FA_ERR_NULL_PTR;
+  if (N > 0 && (k == NULL || v == NULL)) return FA_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4)) return FA_ERR_MISALIGNED;
+  if (N > 0 && (!aligned(k, 16) || !aligned(v, 16))) return FA_ERR_MISALIGNED;
+  {
+    const int64_t lim = (int64_t)1 << 31;
+    int64_t tiles = (M + FA_BLOCK_M - 1) / FA_BLOCK_M;
+    if (M * D >= lim || N * D >= lim) return FA_ERR_TOO_LARGE;
+    if (B > lim / H) return FA_ERR_TOO_LARGE;
+    if (B * H >= lim / tiles) return FA_ERR_TOO_LARGE;
+  }
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H, M, N must be >= 0 and causal 0 or 1";
+    case FA_ERR_BAD_DTYPE: return "FA_ERR_BAD_DTYPE: dtype must be F32, F16 or BF16";
+    case FA_ERR_UNSUPPORTED_D: return "FA_ERR_UNSUPPORTED_D: head dim must be in 1..128";
+    case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite and > 0";
+    case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: q/k/v/o need 16-byte, lse 4-byte alignment";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: per-head extent or grid beyond 32-bit limits";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown fa status";
+  }
+}
+
+int fa_abi_version(void) { return 1; }

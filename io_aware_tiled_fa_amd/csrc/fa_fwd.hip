@@ -1,0 +1,611 @@
+// fa_fwd.hip - FlashAttention forward for CDNA4 (gfx950): kernels and the C-ABI entry.
+//
+// What is computed (per batch b, head h): O = softmax(scale * Q K^T) V and
+// LSE = m + ln(l) per query row, by the online-softmax recurrence over K/V tiles
+// ("Module 08: FlashAttention and Memory-Efficient Kernels", "Tiling and the
+// online softmax"; the loop of the "FlashAttention-style kernel" page): running
+// max m, running sum l, and an un-normalised fp32 accumulator rescaled by
+// alpha = exp2(m_old - m_new), one division at the end.  No M x N matrix exists
+// anywhere; the largest score array is one 32-key x 32-query register tile.
+//
+// Mapping onto gfx950:
+//  * One workgroup = 4 waves = 128 query rows; each wave owns 32 rows.  The Q
+//    rows stay in registers for the whole K/V loop.
+//  * K/V tiles of 64 keys are loaded from HBM with 16-byte coalesced loads,
+//    double-buffered through LDS (one barrier per tile).  V is transposed on its
+//    way into LDS so that every MFMA operand read is one 16-byte LDS read.
+//  * Both products run on MFMA (v_mfma_f32_32x32x16_{bf16,f16}; fp32 inputs use
+//    v_mfma_f32_32x32x2f32).  The kernel computes S^T = K Q^T rather than S: in
+//    the 32x32 accumulator layout each lane then holds 16 keys of ONE query, so
+//    the row max/sum is a register reduction plus one exchange with lane^32, the
+//    rescale of O^T is one multiplier per lane, and P^T is already in the B
+//    operand layout of O^T += V^T P^T (no data movement between the two MFMAs).
+//    The K rows feeding the S^T tile are permuted (bits 2 and 3 of the row index
+//    swapped) so that the 8 keys each lane contributes to a PV MFMA are
+//    consecutive, which makes the V^T operand one contiguous LDS read.
+//  * exp2 with scale*log2(e) folded into one FMA per score; LSE converted back
+//    to natural log once per row ("FlashAttention-style kernel", "The loop").
+//  * Causal (bottom-right, key j visible to row i iff j <= i + N - M): K/V tiles
+//    beyond the workgroup's last visible key are never loaded; a wave skips the
+//    MFMAs of tiles none of its rows can see; masks are applied only on tiles
+//    that cross a row's diagonal or the N tail.  An all-masked running max is
+//    clamped to 0 so that -inf - (-inf) never happens (Module 08, "Common
+//    mistakes"); a row with no visible key ends with l = 0 and stores O = 0,
+//    LSE = -inf.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace {
+
+constexpr int BM = 128;       // query rows per workgroup
+constexpr int BN = 64;        // keys per K/V tile (16/bf16 kernel)
+constexpr int BN32 = 32;      // keys per K/V tile (fp32 kernel)
+constexpr int NTHREADS = 256; // 4 waves of 64
+constexpr float LN2F = 0.693147180559945309417f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct TF16 {
+  using elt = _Float16;
+  using vec8 = f16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+struct TBF16 {
+  using elt = __bf16;
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row of the S^T tile <-> key within a 32-key group: swap bits 2 and 3.
+__device__ __forceinline__ int swap23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Key (relative to the tile's first key, within a 32-key half) held by
+// accumulator register r of a lane in lane-half h.
+__device__ __forceinline__ int key_of_reg(int r, int h) {
+  return 16 * (r >> 3) + 8 * h + (r & 7);
+}
+
+// Which workgroup works on which (batch*head, query tile).  Causal tiles are
+// issued heaviest first (the last query tile sees the most keys).
+struct TileCoord {
+  int bh;
+  int q0;
+};
+template <bool CAUSAL>
+__device__ __forceinline__ TileCoord tile_coord(int qtiles) {
+  int t = blockIdx.x;
+  TileCoord c;
+  c.bh = t / qtiles;
+  int qt = t - c.bh * qtiles;
+  if (CAUSAL) qt = qtiles - 1 - qt;
+  c.q0 = qt * BM;
+  return c;
+}
+
+// Online-softmax update for one lane's query row over NT accumulator tiles of
+// raw scores (already masked with -inf).  m_run is in scaled base-2 units.
+// Returns alpha, updates m_run / l_run, and replaces the scores with p.
+template <int NT>
+__device__ __forceinline__ float softmax_update(f32x16 (&s)[NT], float c, float& m_run,
+                                                float& l_run) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx * c);
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // all masked so far: clamp
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+  float sum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_use));
+      s[t][r] = p;
+      sum += p;
+    }
+  l_run = l_run * alpha + sum;
+  m_run = m_new;
+  return alpha;
+}
+
+// Mask keys a lane's row may not see in the tile starting at key n0.
+// lim: exclusive key limit of the row (min(N, i + N - M + 1) or N).
+template <int NT>
+__device__ __forceinline__ void apply_mask(f32x16 (&s)[NT], int n0, int h, int lim) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = n0 + 32 * t + key_of_reg(r, h);
+      if (key >= lim) s[t][r] = -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp16 / bf16 kernel.  DP: head dim padded to a multiple of 32 (32..128).
+// DFULL: D == DP (rows are whole 16-byte chunks, no column masks).
+template <class T, int DP, bool CAUSAL, bool DFULL>
+__global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
+    const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
+    const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
+    float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+  using elt = typename T::elt;
+  using vec8 = typename T::vec8;
+  constexpr int KSTR = DP + 8;          // LDS row stride of K (elements)
+  constexpr int VSTR = BN + 8;          // LDS row stride of V^T (elements)
+  constexpr int K_ELEMS = BN * KSTR;
+  constexpr int V_ELEMS = DP * VSTR;
+  constexpr int STAGE = K_ELEMS + V_ELEMS;
+  constexpr int KCH = DP / 8;           // 16-byte chunks per K row
+  constexpr int KLD = BN * KCH / NTHREADS;  // K chunks per thread
+  constexpr int NVB = (BN / 8) * (DP / 4);  // 8-key x 4-column V blocks per tile
+  constexpr int DT = DP / 32;           // 32-column O^T tiles
+  constexpr int KK = DP / 16;           // k-steps of S^T
+  static_assert(BN * KCH % NTHREADS == 0, "K staging");
+  static_assert(NVB <= NTHREADS, "V staging");
+
+  __shared__ __attribute__((aligned(16))) elt smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<CAUSAL>(qtiles);
+  const int q0 = tc.q0;
+  const elt* Qh = q + (int64_t)tc.bh * M * D;
+  const elt* Kh = k + (int64_t)tc.bh * N * D;
+  const elt* Vh = v + (int64_t)tc.bh * N * D;
+  elt* Oh = o + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)tc.bh * M;
+
+  const int off = N - M;  // causal: row i sees keys j <= i + off
+  const int qrow = q0 + 32 * w + l32;
+  const int wq_first = q0 + 32 * w;
+  const int wq_last = min(wq_first + 31, M - 1);
+  int n_end = CAUSAL ? min(N, q0 + BM + off) : N;
+  const int ntiles = n_end > 0 ? (n_end + BN - 1) / BN : 0;
+  int w_end = CAUSAL ? min(N, wq_last + 1 + off) : N;
+  if (wq_first >= M) w_end = 0;
+  const int lim = CAUSAL ? min(N, qrow + off + 1) : N;
+
+  // Q^T as the B operand of S^T = K Q^T: lane holds row qrow, 8 features per k-step.
+  vec8 qreg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int d0 = 16 * kk + 8 * h;
+    if (DFULL) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qrow < M) raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + d0);
+      qreg[kk] = __builtin_bit_cast(vec8, raw);
+    } else {
+      vec8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = (qrow < M && d0 + e < D) ? Qh[(int64_t)qrow * D + d0 + e] : (elt)0.0f;
+      qreg[kk] = x;
+    }
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  // Register staging of one K/V tile (global -> registers -> LDS).
+  u32x4 kreg[KLD];
+  u32x2 vreg[8];
+  const int vb_kg = tid / (DP / 4);
+  const int vb_dc = tid - vb_kg * (DP / 4);
+
+  auto load_tile = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int ci = tid + NTHREADS * i;
+      const int row = ci / KCH;
+      const int col = (ci - row * KCH) * 8;
+      const int key = n0 + row;
+      if (DFULL) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (key < N) raw = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
+        kreg[i] = raw;
+      } else {
+        vec8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e] = (key < N && col + e < D) ? Kh[(int64_t)key * D + col + e] : (elt)0.0f;
+        kreg[i] = __builtin_bit_cast(u32x4, x);
+      }
+    }
+    if (tid < NVB) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int key = n0 + 8 * vb_kg + kk;
+        const int d0 = 4 * vb_dc;
+        if (DFULL) {
+          u32x2 raw = {0u, 0u};
+          if (key < N) raw = *reinterpret_cast<const u32x2*>(Vh + (int64_t)key * D + d0);
+          vreg[kk] = raw;
+        } else {
+          elt x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = (key < N && d0 + e < D) ? Vh[(int64_t)key * D + d0 + e] : (elt)0.0f;
+          vreg[kk] = __builtin_bit_cast(u32x2, x);
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int stage) {
+    elt* Ks = smem + stage * STAGE;
+    elt* Vs = Ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int ci = tid + NTHREADS * i;
+      const int row = ci / KCH;
+      const int col = (ci - row * KCH) * 8;
+      *reinterpret_cast<u32x4*>(Ks + row * KSTR + col) = kreg[i];
+    }
+    if (tid < NVB) {
+      // 8 keys x 4 columns -> 4 rows of V^T with 8 consecutive keys each.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 out;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          out[m] = __builtin_amdgcn_perm(vreg[2 * m + 1][j >> 1], vreg[2 * m][j >> 1], sel);
+        *reinterpret_cast<u32x4*>(Vs + (4 * vb_dc + j) * VSTR + 8 * vb_kg) = out;
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const int krow0 = swap23(l32);
+  for (int j = 0; j < ntiles; ++j) {
+    const int n0 = j * BN;
+    const bool more = j + 1 < ntiles;
+    if (more) load_tile(n0 + BN);
+    if (n0 < w_end) {
+      const elt* Ks = smem + (j & 1) * STAGE;
+      const elt* Vs = Ks + K_ELEMS;
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const vec8 a0 = *reinterpret_cast<const vec8*>(Ks + krow0 * KSTR + 16 * kk + 8 * h);
+        const vec8 a1 =
+            *reinterpret_cast<const vec8*>(Ks + (32 + krow0) * KSTR + 16 * kk + 8 * h);
+        s[0] = T::mfma(a0, qreg[kk], s[0]);
+        s[1] = T::mfma(a1, qreg[kk], s[1]);
+      }
+      const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
+      if (need_mask) apply_mask<2>(s, n0, h, lim);
+      const float alpha = softmax_update<2>(s, c, m_run, l_run);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        f32x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = s[cc >> 1][8 * (cc & 1) + e];
+        const vec8 pb = __builtin_convertvector(pf, vec8);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const vec8 a =
+              *reinterpret_cast<const vec8*>(Vs + (32 * dt + l32) * VSTR + 16 * cc + 8 * h);
+          acc[dt] = T::mfma(a, pb, acc[dt]);
+        }
+      }
+    }
+    if (more) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m + log2 l).
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qrow < M) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        elt y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (elt)(acc[dt][4 * g + e] * inv);
+        if (DFULL) {
+          *reinterpret_cast<u32x2*>(Oh + (int64_t)qrow * D + d0) = __builtin_bit_cast(u32x2, y);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (d0 + e < D) Oh[(int64_t)qrow * D + d0 + e] = y[e];
+        }
+      }
+    if (h == 0)
+      Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same structure on v_mfma_f32_32x32x2f32 with P kept in fp32.
+// 32-key tiles; K rows in LDS at an odd stride (conflict-free column reads),
+// V row-major (the V^T operand of a 2-key step is one row of 32 columns).
+template <int DP, bool CAUSAL, bool DFULL>
+__global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+  constexpr int KSTR = DP + 1;
+  constexpr int VSTR = DP + 4;
+  constexpr int K_ELEMS = BN32 * KSTR;
+  constexpr int V_ELEMS = BN32 * VSTR;
+  constexpr int STAGE = K_ELEMS + V_ELEMS;
+  constexpr int CH = DP / 4;                    // 16-byte chunks per row
+  constexpr int LD = (BN32 * CH + NTHREADS - 1) / NTHREADS;
+  constexpr int DT = DP / 32;
+  constexpr int KS = DP / 2;                    // k-steps of S^T
+
+  __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<CAUSAL>(qtiles);
+  const int q0 = tc.q0;
+  const float* Qh = q + (int64_t)tc.bh * M * D;
+  const float* Kh = k + (int64_t)tc.bh * N * D;
+  const float* Vh = v + (int64_t)tc.bh * N * D;
+  float* Oh = o + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)tc.bh * M;
+
+  const int off = N - M;
+  const int qrow = q0 + 32 * w + l32;
+  const int wq_first = q0 + 32 * w;
+  const int wq_last = min(wq_first + 31, M - 1);
+  const int n_end = CAUSAL ? min(N, q0 + BM + off) : N;
+  const int ntiles = n_end > 0 ? (n_end + BN32 - 1) / BN32 : 0;
+  int w_end = CAUSAL ? min(N, wq_last + 1 + off) : N;
+  if (wq_first >= M) w_end = 0;
+  const int lim = CAUSAL ? min(N, qrow + off + 1) : N;
+
+  float qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int d = 2 * s + h;
+    qreg[s] = (qrow < M && d < D) ? Qh[(int64_t)qrow * D + d] : 0.0f;
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  float4 kr[LD], vr[LD];
+  auto load_tile = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int ci = tid + NTHREADS * i;
+      const int row = ci / CH;
+      const int col = (ci - row * CH) * 4;
+      const int key = n0 + row;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (ci < BN32 * CH && key < N) {
+        if (DFULL) {
+          a = *reinterpret_cast<const float4*>(Kh + (int64_t)key * D + col);
+          b = *reinterpret_cast<const float4*>(Vh + (int64_t)key * D + col);
+        } else {
+          const float* kp = Kh + (int64_t)key * D;
+          const float* vp = Vh + (int64_t)key * D;
+          a.x = col + 0 < D ? kp[col + 0] : 0.f;
+          a.y = col + 1 < D ? kp[col + 1] : 0.f;
+          a.z = col + 2 < D ? kp[col + 2] : 0.f;
+          a.w = col + 3 < D ? kp[col + 3] : 0.f;
+          b.x = col + 0 < D ? vp[col + 0] : 0.f;
+          b.y = col + 1 < D ? vp[col + 1] : 0.f;
+          b.z = col + 2 < D ? vp[col + 2] : 0.f;
+          b.w = col + 3 < D ? vp[col + 3] : 0.f;
+        }
+      }
+      kr[i] = a;
+      vr[i] = b;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    float* Ks = smem + stage * STAGE;
+    float* Vs = Ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int ci = tid + NTHREADS * i;
+      if (ci < BN32 * CH) {
+        const int row = ci / CH;
+        const int col = (ci - row * CH) * 4;
+        float* kp = Ks + row * KSTR + col;
+        kp[0] = kr[i].x;
+        kp[1] = kr[i].y;
+        kp[2] = kr[i].z;
+        kp[3] = kr[i].w;
+        *reinterpret_cast<float4*>(Vs + row * VSTR + col) = vr[i];
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const int krow = swap23(l32);
+  for (int j = 0; j < ntiles; ++j) {
+    const int n0 = j * BN32;
+    const bool more = j + 1 < ntiles;
+    if (more) load_tile(n0 + BN32);
+    if (n0 < w_end) {
+      const float* Ks = smem + (j & 1) * STAGE;
+      const float* Vs = Ks + K_ELEMS;
+      f32x16 s[1] = {f32x16{}};
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[krow * KSTR + 2 * st + h], qreg[st], s[0],
+                                                    0, 0, 0);
+      const bool need_mask = (n0 + BN32 > N) || (CAUSAL && n0 + BN32 - 1 > wq_first + off);
+      if (need_mask) apply_mask<1>(s, n0, h, lim);
+      const float alpha = softmax_update<1>(s, c, m_run, l_run);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key_of_reg(r, h);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VSTR + 32 * dt + l32], s[0][r],
+                                                         acc[dt], 0, 0, 0);
+      }
+    }
+    if (more) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qrow < M) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        if (DFULL) {
+          float4 y = make_float4(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
+                                 acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+          *reinterpret_cast<float4*>(Oh + (int64_t)qrow * D + d0) = y;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (d0 + e < D) Oh[(int64_t)qrow * D + d0 + e] = acc[dt][4 * g + e] * inv;
+        }
+      }
+    if (h == 0)
+      Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host dispatch.
+
+struct Launch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int M, N, D, qtiles;
+  float c;
+  dim3 grid;
+  hipStream_t stream;
+};
+
+template <class T, int DP, bool CAUSAL>
+void launch_lp(const Launch& a) {
+  using elt = typename T::elt;
+  const bool full = a.D == DP;
+  if (full)
+    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, true>), a.grid, dim3(NTHREADS), 0,
+                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
+                       a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+  else
+    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, false>), a.grid, dim3(NTHREADS), 0,
+                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
+                       a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+}
+
+template <int DP, bool CAUSAL>
+void launch_f32(const Launch& a) {
+  if (a.D == DP)
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, true>), a.grid, dim3(NTHREADS), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+  else
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, false>), a.grid, dim3(NTHREADS), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+}
+
+template <class T, bool CAUSAL>
+void dispatch_lp(const Launch& a) {
+  if (a.D <= 32) launch_lp<T, 32, CAUSAL>(a);
+  else if (a.D <= 64) launch_lp<T, 64, CAUSAL>(a);
+  else if (a.D <= 96) launch_lp<T, 96, CAUSAL>(a);
+  else launch_lp<T, 128, CAUSAL>(a);
+}
+
+template <bool CAUSAL>
+void dispatch_f32(const Launch& a) {
+  if (a.D <= 32) launch_f32<32, CAUSAL>(a);
+  else if (a.D <= 64) launch_f32<64, CAUSAL>(a);
+  else if (a.D <= 96) launch_f32<96, CAUSAL>(a);
+  else launch_f32<128, CAUSAL>(a);
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                      int causal, int dtype, void* stream) {
+  const int st = fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (B == 0 || H == 0 || M == 0) return FA_OK;
+  Launch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.D = (int)D;
+  a.qtiles = (int)((M + BM - 1) / BM);
+  // scale * log2(e) folded once (in double, rounded to fp32) so every exponential is exp2.
+  a.c = (float)((double)scale * 1.4426950408889634074);
+  a.grid = dim3((unsigned)(B * H * a.qtiles));
+  a.stream = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear a stale error so the check below is about this launch
+  switch (dtype) {
+    case FA_DTYPE_F16:
+      causal ? dispatch_lp<TF16, true>(a) : dispatch_lp<TF16, false>(a);
+      break;
+    case FA_DTYPE_BF16:
+      causal ? dispatch_lp<TBF16, true>(a) : dispatch_lp<TBF16, false>(a);
+      break;
+    default:
+      causal ? dispatch_f32<true>(a) : dispatch_f32<false>(a);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

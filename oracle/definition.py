@@ -80,7 +80,7 @@ def masked_softmax(S: np.ndarray, vis: np.ndarray):
     lse = -inf (the clamped-max reading described in the module docstring).
     """
     Sm = np.where(vis, S, -np.inf)
-    m = Sm.max(axis=1)
+    m = np.max(Sm, axis=1, initial=-np.inf)  # N = 0 leaves every row empty
     empty = ~vis.any(axis=1)
     m_safe = np.where(empty, 0.0, m)
     e = np.where(vis, np.exp(Sm - m_safe[:, None]), 0.0)
@@ -123,9 +123,10 @@ def attention(q, k, v, scale: float, causal: bool = False, return_sp: bool = Fal
     lead = q.shape[:-2]
     M, D = q.shape[-2:]
     N = k.shape[-2]
-    qf = q.reshape(-1, M, D)
-    kf = k.reshape(-1, N, k.shape[-1])
-    vf = v.reshape(-1, N, v.shape[-1])
+    nh = int(np.prod(lead, dtype=np.int64))
+    qf = q.reshape(nh, M, D)
+    kf = k.reshape(nh, N, k.shape[-1])
+    vf = v.reshape(nh, N, v.shape[-1])
     Dv = vf.shape[-1]
     O = np.empty((qf.shape[0], M, Dv))
     L = np.empty((qf.shape[0], M))

@@ -265,6 +265,10 @@ def pin_empty_rows():
     assert np.all(np.isfinite(L[M - N:]))
     # the first non-empty row sees exactly key 0
     assert np.abs(O[M - N] - v[0]).max() <= 1e-15
+    # no keys at all: every row is empty, causal or not
+    for causal in (False, True):
+        O0, L0 = attention(q, np.zeros((0, 3)), np.zeros((0, 3)), 1.0, causal)
+        assert np.all(O0 == 0.0) and np.all(np.isneginf(L0))
 
 
 def pin_shift_feature():

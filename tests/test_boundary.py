@@ -1,0 +1,103 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects every bad argument on the host before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import io_aware_tiled_fa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, DTYPE, BAD_D, SCALE, ALIGN, LARGE, HIP = range(9)
+P = 0x10000  # a 16-byte aligned fake address (never dereferenced: validation only)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    names = _declared_functions()
+    assert set(names) >= {"fa_fwd", "fa_check_args", "fa_status_string", "fa_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert fa.fa_abi_version() == 1
+
+
+def test_status_strings():
+    for code, name in fa.STATUS.items():
+        assert fa.fa_status_string(code).startswith(name)
+    assert "unknown" in fa.fa_status_string(99)
+
+
+def _chk(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, M=100, N=70, D=64, scale=0.125, causal=0,
+             dtype=fa.DTYPE_BF16)
+    a.update(kw)
+    return fa.fa_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["M"],
+                            a["N"], a["D"], a["scale"], a["causal"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, OK),
+    ({"dtype": 3}, DTYPE), ({"dtype": -1}, DTYPE),
+    ({"B": -1}, SHAPE), ({"H": -2}, SHAPE), ({"M": -1}, SHAPE), ({"N": -5}, SHAPE),
+    ({"causal": 2}, SHAPE),
+    ({"D": 0}, BAD_D), ({"D": 129}, BAD_D), ({"D": -3}, BAD_D), ({"D": 1}, OK), ({"D": 128}, OK),
+    ({"scale": 0.0}, SCALE), ({"scale": -0.1}, SCALE), ({"scale": math.inf}, SCALE),
+    ({"scale": math.nan}, SCALE),
+    ({"q": 0}, NULL), ({"o": 0}, NULL), ({"lse": 0}, NULL), ({"k": 0}, NULL), ({"v": 0}, NULL),
+    ({"q": P + 8}, ALIGN), ({"k": P + 2}, ALIGN), ({"o": P + 4}, ALIGN), ({"lse": P + 2}, ALIGN),
+    ({"lse": P + 4}, OK),
+    ({"B": 0, "q": 0, "k": 0, "v": 0, "o": 0, "lse": 0}, OK),   # empty: nothing to do
+    ({"M": 0, "q": 0, "o": 0, "lse": 0}, OK),
+    ({"N": 0, "k": 0, "v": 0}, OK),                             # no keys: every row empty
+    ({"M": 1 << 25, "D": 64}, LARGE), ({"N": 1 << 25, "D": 64}, LARGE),
+    ({"B": 1 << 20, "H": 1 << 12, "M": 128}, LARGE),
+])
+def test_check_args(kw, code):
+    assert _chk(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 7}, DTYPE), ({"D": 200}, BAD_D), ({"scale": -1.0}, SCALE), ({"q": 0}, NULL),
+    ({"q": P + 8}, ALIGN), ({"B": 0}, OK), ({"M": 0}, OK),
+])
+def test_fa_fwd_rejects_before_any_hip_call(kw, code):
+    # Every case here returns from host validation (or is an empty problem) and
+    # never reaches the HIP runtime, so it runs without a GPU.
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, M=100, N=70, D=64, scale=0.125, causal=1,
+             dtype=fa.DTYPE_F16)
+    a.update(kw)
+    st = fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["M"], a["N"],
+                   a["D"], a["scale"], a["causal"], a["dtype"], None)
+    assert st == code
+
+
+def test_python_wrapper_validates_before_the_library(monkeypatch):
+    import torch
+
+    q = torch.zeros(1, 1, 4, 8)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)  # CPU tensors are refused
+    with pytest.raises(ValueError):
+        fa.fwd(q[0], q[0], q[0])
+    with pytest.raises(TypeError):
+        fa._dtype_code(torch.zeros(1, dtype=torch.int32))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "lib_path", lambda: str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        fa.load()
+    with pytest.raises(ImportError):
+        fa.fa_fwd(P, P, P, P, P, 1, 1, 1, 1, 8, 1.0, 0, 0, None)

@@ -1,0 +1,209 @@
+"""Edge cases of the HIP path through the C ABI: head dims, tails, empty rows and
+inputs, closed forms that need no oracle, invariances, determinism."""
+
+import math
+
+import numpy as np
+import pytest
+
+import io_aware_tiled_fa_amd as fa
+import oracle
+from parity import TOL_LSE, TOL_O, check
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TDT = None
+
+
+def _t():
+    import torch
+
+    return torch
+
+
+def _dt(name):
+    torch = _t()
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+def _say(msg):
+    print(f"CASE {msg}", flush=True)
+
+
+def _inputs(B, H, M, N, D, dtype, seed, q_mult=1.0):
+    w = Workload("edge", B, H, M, N, D, dtype, False, 1 / math.sqrt(D), seed, q_mult)
+    return make_inputs(w)
+
+
+def _fwd(q, k, v, causal, scale):
+    torch = _t()
+    dev = torch.device("cuda:0")
+    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_native_library_is_the_one_loaded():
+    fa.load()
+    maps = open("/proc/self/maps").read()
+    assert fa.lib_path() in maps
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [1, 8, 32, 40, 64, 65, 96, 100, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_and_tails(dtype, D, causal):
+    M, N = 77, 150 if not causal else 77
+    if causal and D % 2:
+        M, N = 150, 77  # M > N: empty rows too
+    _say(f"dims dtype={dtype} D={D} causal={causal} M={M} N={N}")
+    q, k, v = _inputs(2, 3, M, N, D, dtype, 100 + D)
+    s = 1 / math.sqrt(D)
+    o, lse = _fwd(q, k, v, causal, s)
+    O_ref, L_ref = oracle.attention(q, k, v, s, causal)
+    check(f"edge_{dtype}_D{D}_c{int(causal)}", dtype, o.double().cpu().numpy(),
+          lse.cpu().numpy(), O_ref, L_ref)
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (1, 300), (129, 65), (128, 64), (257, 1000), (1000, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tile_boundaries(M, N, causal):
+    _say(f"tiles M={M} N={N} causal={causal}")
+    q, k, v = _inputs(1, 2, M, N, 64, "bf16", 7)
+    o, lse = _fwd(q, k, v, causal, 0.125)
+    O_ref, L_ref = oracle.attention(q, k, v, 0.125, causal)
+    check(f"tiles_{M}x{N}_c{int(causal)}", "bf16", o.double().cpu().numpy(), lse.cpu().numpy(),
+          O_ref, L_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_key_is_exact(dtype):
+    """N = 1: the only weight is 1, so O = V_0 and LSE = scale * q.k_0.  For fp16 and
+    bf16 outputs O equals V_0 bit for bit (the fp32 result acc * (1/l) is within an
+    ulp or two of V_0 and rounds back to it); in fp32 that ulp shows."""
+    _say(f"N=1 dtype={dtype}")
+    q, k, v = _inputs(2, 2, 100, 1, 64, dtype, 8)
+    o, lse = _fwd(q, k, v, False, 0.125)
+    torch = _t()
+    want = v.expand(-1, -1, 100, -1).contiguous()
+    if dtype == "f32":
+        assert torch.allclose(o.cpu(), want, rtol=4e-7, atol=0)
+    else:
+        assert torch.equal(o.cpu(), want)
+    L_ref = 0.125 * np.einsum("bhmd,bhd->bhm", q.double().numpy(), k[:, :, 0].double().numpy())
+    assert np.abs(lse.cpu().numpy() - L_ref).max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_give_mean_of_visible_values(causal):
+    """K = 0: every score is 0, O is the mean of the visible V rows, LSE = ln(#visible)."""
+    torch = _t()
+    M, N = 90, 200
+    _say(f"K=0 causal={causal}")
+    q, k, v = _inputs(1, 2, M, N, 64, "f16", 9)
+    k = torch.zeros_like(k)
+    o, lse = _fwd(q, k, v, causal, 0.125)
+    vv = v.double().numpy()
+    for i in [0, 1, 45, 89]:
+        n = N if not causal else i + N - M + 1
+        assert np.abs(o[0, :, i].double().cpu().numpy() - vv[0, :, :n].mean(axis=1)).max() <= 2e-3 + 1e-3
+        assert np.abs(lse[0, :, i].cpu().numpy() - math.log(n)).max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_rows_and_no_keys(dtype):
+    """Causal M > N: rows i < M - N see nothing -> O == 0 exactly and LSE == -inf;
+    N == 0: every row is empty."""
+    torch = _t()
+    _say(f"empty rows dtype={dtype}")
+    q, k, v = _inputs(1, 2, 300, 100, 32, dtype, 10)
+    o, lse = _fwd(q, k, v, True, 0.2)
+    assert torch.all(o[:, :, :200].cpu() == 0) and torch.all(torch.isneginf(lse[:, :, :200].cpu()))
+    O_ref, L_ref = oracle.attention(q, k, v, 0.2, True)
+    check(f"empty_rows_{dtype}", dtype, o.double().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref)
+    dev = torch.device("cuda:0")
+    q0 = q.to(dev)
+    kv0 = torch.empty((1, 2, 0, 32), dtype=q.dtype, device=dev)
+    o0 = torch.full_like(q0, 7.0)
+    l0 = torch.zeros((1, 2, 300), device=dev)
+    fa.fwd(q0, kv0, kv0, causal=False, scale=0.2, out=o0, lse=l0)
+    torch.cuda.synchronize()
+    assert torch.all(o0 == 0) and torch.all(torch.isneginf(l0))
+
+
+def test_empty_problems_touch_nothing():
+    torch = _t()
+    _say("empty problems")
+    dev = torch.device("cuda:0")
+    for shape_q, shape_k in [((0, 2, 10, 16), (0, 2, 10, 16)), ((1, 2, 0, 16), (1, 2, 10, 16))]:
+        q = torch.zeros(shape_q, device=dev, dtype=torch.float16)
+        k = torch.zeros(shape_k, device=dev, dtype=torch.float16)
+        o, lse = fa.fwd(q, k, k)
+        torch.cuda.synchronize()
+        assert o.numel() == 0 and lse.numel() == 0
+
+
+def test_shift_feature_and_padding():
+    """Appending Q' = [Q | 1], K' = [K | 4] adds 4*scale to every score: O unchanged,
+    LSE + 4*scale (also runs D = 97 through the padded path).  D = 96 data against
+    the same data zero-padded to 128: same O in the first 96 columns, zeros after."""
+    torch = _t()
+    _say("shift feature / padding")
+    q, k, v = _inputs(2, 2, 200, 300, 96, "bf16", 11)
+    s = 0.1
+    o, lse = _fwd(q, k, v, True, s)
+    one = torch.ones(*q.shape[:-1], 1, dtype=q.dtype)
+    four = torch.full((*k.shape[:-1], 1), 4.0, dtype=k.dtype)
+    v97 = torch.cat([v, torch.zeros(*v.shape[:-1], 1, dtype=v.dtype)], -1)
+    o2, lse2 = _fwd(torch.cat([q, one], -1), torch.cat([k, four], -1), v97, True, s)
+    assert np.abs(o2[..., :96].double().cpu().numpy() - o.double().cpu().numpy()).max() <= 2 * TOL_O["bf16"]
+    assert torch.all(o2[..., 96:].cpu() == 0)
+    s32 = float(np.float32(s))
+    assert np.abs(lse2.cpu().numpy() - lse.cpu().numpy() - 4 * s32).max() <= 2 * TOL_LSE
+    pad = lambda x: torch.cat([x, torch.zeros(*x.shape[:-1], 32, dtype=x.dtype)], -1)  # noqa: E731
+    o3, lse3 = _fwd(pad(q), pad(k), pad(v), True, s)
+    assert torch.equal(o3[..., :96].cpu(), o.cpu()) and torch.all(o3[..., 96:].cpu() == 0)
+    assert torch.equal(lse3.cpu(), lse.cpu())
+
+
+def test_permutation_invariance():
+    torch = _t()
+    _say("permutation")
+    q, k, v = _inputs(1, 3, 128, 500, 128, "f16", 12, q_mult=4.0)
+    o, lse = _fwd(q, k, v, False, 1 / math.sqrt(128))
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(500))
+    o2, lse2 = _fwd(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), False, 1 / math.sqrt(128))
+    assert np.abs(o.double().cpu().numpy() - o2.double().cpu().numpy()).max() <= 2 * TOL_O["f16"]
+    assert np.abs(lse.cpu().numpy() - lse2.cpu().numpy()).max() <= TOL_LSE
+
+
+def test_future_keys_do_not_leak():
+    """Causal: changing keys/values no row <= i0 can see leaves those rows bit-identical."""
+    torch = _t()
+    _say("future leak")
+    M = N = 512
+    q, k, v = _inputs(1, 2, M, N, 64, "bf16", 13)
+    o, lse = _fwd(q, k, v, True, 0.125)
+    i0 = 300
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, i0 + 1:] = 3.0
+    v2[:, :, i0 + 1:] = -5.0
+    o2, lse2 = _fwd(q, k2, v2, True, 0.125)
+    assert torch.equal(o[:, :, : i0 + 1].cpu(), o2[:, :, : i0 + 1].cpu())
+    assert torch.equal(lse[:, :, : i0 + 1].cpu(), lse2[:, :, : i0 + 1].cpu())
+    assert not torch.equal(o[:, :, -1].cpu(), o2[:, :, -1].cpu())
+
+
+def test_deterministic_and_stream():
+    torch = _t()
+    _say("determinism / stream")
+    q, k, v = _inputs(2, 4, 700, 900, 128, "bf16", 14)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o1, l1 = fa.fwd(qd, kd, vd, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = fa.fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
