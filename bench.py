@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of the attention forward pass (fa_fwd) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one fa_fwd call over the whole batch of the workload: the complete
+hot path (Q tile load, K/V streaming through LDS, both MFMA products, online
+softmax, epilogue) with Q, K and V already resident in HBM.  W untimed warmup
+steps, then exactly K timed steps between two device synchronisations.  One JSON
+line goes to stdout; progress goes to stderr.
+
+FLOP accounting: the headline value uses 4*B*H*M*N*D, halved for causal.  The
+roofline object uses the algorithmic count, 4*D FLOP per visible (query, key)
+pair, over the average duration of one launch measured with HIP events on the
+stream the kernel runs on.  Peak: MI355X dense bf16/fp16 MFMA 2516.6 TFLOP/s
+(fp32 MFMA 157.3 TFLOP/s for fp32 inputs).
+
+The cpu_baseline object times the fp64 CPU oracle (untuned) on a bounded sample
+of the same workload (whole heads, all rows) on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import (BENCH_WORKLOAD, WORKLOADS, compulsory_bytes, exact_flops,  # noqa: E402
+                       make_inputs, metric_flops)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+METRIC = "attn fwd TFLOP/s + % of MI355X MFMA peak (N=4096 d=128 causal bf16)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, qc, kc, vc, budget_s: float = 15.0, max_heads: int = 32):
+    """Time the fp64 oracle on whole heads of the workload until ~budget_s."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    qf = qc.reshape(-1, w.M, w.D)
+    kf = kc.reshape(-1, w.N, w.D)
+    vf = vc.reshape(-1, w.N, w.D)
+    # widen one head at a time inside the timed loop (part of the oracle's work)
+    t0 = time.perf_counter()
+    done = 0
+    for h in range(min(max_heads, qf.shape[0])):
+        oracle.attention(qf[h], kf[h], vf[h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    fl = metric_flops(1, done, w.M, w.N, w.D, w.causal)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} heads, all {w.M} rows, fp64 numpy, "
+                  f"{dt:.1f} s wall ({os.cpu_count()} cpus visible)",
+    }
+
+
+def load_traffic(w, kernel_ms):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(w.name)
+    except Exception:  # noqa: BLE001
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc", "fa_fwd.hip")
+    import hashlib
+
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("source_sha256_16") != digest:
+        return None  # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=BENCH_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward path here has no "
+              "multi-GPU mode (each (batch, head) is independent; see the sharding notes in "
+              "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import io_aware_tiled_fa_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load()
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {w}")
+    qc, kc, vc = make_inputs(w)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = {"f32": fa.DTYPE_F32, "f16": fa.DTYPE_F16, "bf16": fa.DTYPE_BF16}[w.dtype]
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+
+    def step():
+        st = fa.fa_fwd(*ptrs, w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code,
+                       stream.cuda_stream)
+        if st != 0:
+            raise fa.FaError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / K
+    avg_launch_ms = sum(launch_ms) / K
+    med_launch_ms = sorted(launch_ms)[K // 2]
+
+    fl_metric = metric_flops(w.B, w.H, w.M, w.N, w.D, w.causal)
+    fl_exact = exact_flops(w.B, w.H, w.M, w.N, w.D, w.causal)
+    tflops = fl_metric / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = fl_exact / (avg_launch_ms * 1e-3) / 1e12
+    traffic = load_traffic(w, avg_launch_ms)
+    log(f"ms/step {ms_per_step:.4f}  avg launch {avg_launch_ms:.4f} ms  median {med_launch_ms:.4f} ms  "
+        f"{tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)  wall {wall:.3f}s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), see workloads)",
+        "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "M": w.M, "N": w.N, "D": w.D,
+            "causal": w.causal, "scale": w.scale, "flop_metric": fl_metric,
+            "flop_visible_pairs": fl_exact, "compulsory_bytes": compulsory_bytes(w),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel": "fa_fwd_lp_kernel" if w.dtype != "f32" else "fa_fwd_f32_kernel",
+            "avg_launch_ms": round(avg_launch_ms, 5),
+            "hbm_gbs_compulsory": round(compulsory_bytes(w) / (avg_launch_ms * 1e-3) / 1e9, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(w, qc, kc, vc, budget_s=args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

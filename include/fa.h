@@ -77,6 +77,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            float scale, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_general - the same operation, arguments, ownership and errors as
+ * fa_fwd, always executed by the general kernel (K/V tiles staged through
+ * registers, any D in 1..128) instead of the direct-to-LDS fast path fa_fwd
+ * picks for fp16/bf16 with D in {64, 96, 128}.  Results agree with fa_fwd
+ * within the accuracy stated for the dtype (the summation order is the same,
+ * so they are usually bit-identical); it exists to cross-check the two paths.
+ */
+int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                   float scale, int causal, int dtype, void* stream);
+
+/*
  * fa_check_args - the host-side validation fa_fwd performs, with the same
  * arguments and return codes, and no HIP call (usable without a GPU).
  */

@@ -15,7 +15,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_check_args", "fa_status_string",
+__all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_fwd_general", "fa_check_args", "fa_status_string",
            "fa_abi_version", "fwd", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "STATUS"]
 
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
@@ -53,6 +53,8 @@ def load():
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp, ctypes.c_int,
                            ctypes.c_int, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_general.argtypes = lib.fa_fwd.argtypes
+    lib.fa_fwd_general.restype = ctypes.c_int
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp,
                                   ctypes.c_int, ctypes.c_int]
     lib.fa_check_args.restype = ctypes.c_int
@@ -68,6 +70,12 @@ def fa_fwd(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream=None) ->
     """Direct call of the C entry point; pointers are integer device addresses."""
     return load().fa_fwd(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal), int(dtype),
                          stream)
+
+
+def fa_fwd_general(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream=None) -> int:
+    """Direct call of the C entry point that always runs the general kernel."""
+    return load().fa_fwd_general(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal),
+                                 int(dtype), stream)
 
 
 def fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype) -> int:
@@ -93,11 +101,12 @@ def _dtype_code(t):
 
 
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
-        stream=None):
+        stream=None, general: bool = False):
     """O, LSE = attention forward of q [B,H,M,D], k/v [B,H,N,D] (device tensors).
 
     Allocates ``o`` (like q) and ``lse`` ([B,H,M] fp32) unless given, enqueues
     fa_fwd on ``stream`` (default: torch's current stream) and returns them.
+    ``general=True`` calls fa_fwd_general instead.
     """
     import torch
 
@@ -125,7 +134,8 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+    entry = fa_fwd_general if general else fa_fwd
+    st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, H, M, N, D, scale, 1 if causal else 0, code, stream)
     if st != 0:
         raise FaError(st)

@@ -95,6 +95,19 @@ __device__ __forceinline__ TileCoord tile_coord(int qtiles) {
   return c;
 }
 
+// Lanes l and l^32 hold the same query row (different keys).  v_permlane32_swap
+// exchanges the two wave halves in one VALU op (no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Online-softmax update for one lane's query row over NT accumulator tiles of
 // raw scores (already masked with -inf).  m_run is in scaled base-2 units.
 // Returns alpha, updates m_run / l_run, and replaces the scores with p.
@@ -106,7 +119,7 @@ __device__ __forceinline__ float softmax_update(f32x16 (&s)[NT], float c, float&
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = pair_max(mx);
   const float m_new = fmaxf(m_run, mx * c);
   const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // all masked so far: clamp
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -326,7 +339,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
   }
 
   // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m + log2 l).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qrow < M) {
 #pragma unroll
@@ -344,6 +357,201 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
           for (int e = 0; e < 4; ++e)
             if (d0 + e < D) Oh[(int64_t)qrow * D + d0 + e] = y[e];
         }
+      }
+    if (h == 0)
+      Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// fp16 / bf16 fast path for D in {64, 96, 128}: K and V tiles are copied from
+// HBM straight into LDS (global_load_lds, 16 B per lane, no VGPR staging), in
+// their natural row-major layout with a per-row XOR swizzle of the 16-byte
+// chunks.  The K operand of S^T is one ds_read_b128 per lane and k-step; the
+// V^T operand of O^T is read transposed out of row-major V with two
+// ds_read_b64_tr_b16 per MFMA (each lane of a 16-lane group receives one
+// column of a 4-row x 4-column block).  The swizzle makes both read patterns
+// bank-conflict free: 16 consecutive rows hit 16 distinct chunk positions for
+// the K reads, and the 4 rows of a transpose read land in 4 distinct 64-byte
+// groups of banks.
+template <int DP>
+struct FastLayout {
+  static constexpr int ROWB = DP == 64 ? 128 : 256;  // LDS bytes per K/V row
+  static constexpr int CPR = DP / 8;                  // 16-byte chunks holding data
+  static constexpr int SLOTS = ROWB / 16;             // 16-byte slots per row
+  static constexpr int TILEB = BN * ROWB;             // one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
+  static constexpr int RPB = 1024 / ROWB;             // rows per 1 KB copy instruction
+  static constexpr int NBLK = TILEB / 1024;           // copy instructions per tile matrix
+  // physical slot of logical chunk c in row r is c ^ swz(r)
+  static __device__ __forceinline__ int swz(int r) {
+    return DP == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+  }
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ void copy16_to_lds(const void* g, char* lds_block) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds_block, 16, 0, 0);
+}
+
+template <class T, int DP, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_fast_kernel(
+    const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
+    const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
+    float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+  using elt = typename T::elt;
+  using vec8 = typename T::vec8;
+  using L = FastLayout<DP>;
+  constexpr int DT = DP / 32;
+  constexpr int KK = DP / 16;
+  constexpr int BPW = L::NBLK / 4;  // copy instructions per wave per tile matrix
+
+  __shared__ __attribute__((aligned(1024))) char lds0[L::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char lds1[L::STAGEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<CAUSAL>(qtiles);
+  const int q0 = tc.q0;
+  const elt* Qh = q + (int64_t)tc.bh * M * D;
+  const elt* Kh = k + (int64_t)tc.bh * N * D;
+  const elt* Vh = v + (int64_t)tc.bh * N * D;
+  elt* Oh = o + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)tc.bh * M;
+
+  const int off = N - M;
+  const int qrow = q0 + 32 * w + l32;
+  const int wq_first = q0 + 32 * w;
+  const int wq_last = min(wq_first + 31, M - 1);
+  const int n_end = CAUSAL ? min(N, q0 + BM + off) : N;
+  const int ntiles = n_end > 0 ? (n_end + BN - 1) / BN : 0;
+  int w_end = CAUSAL ? min(N, wq_last + 1 + off) : N;
+  if (wq_first >= M) w_end = 0;
+  const int lim = CAUSAL ? min(N, qrow + off + 1) : N;
+
+  vec8 qreg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qrow < M) raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * kk + 8 * h);
+    qreg[kk] = __builtin_bit_cast(vec8, raw);
+  }
+
+  // Per-lane copy plan: slot `lane` of each 1 KB block holds logical chunk
+  // (lane % SLOTS) ^ swz(row) of row (blk * RPB + lane / SLOTS).
+  const int cp_sub = lane / L::SLOTS;
+  const int cp_slot = lane % L::SLOTS;
+  auto issue_tile = [&](int n0, char* stage) {
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      const int blk = w * BPW + b;
+      const int row = blk * L::RPB + cp_sub;
+      const int chunk = cp_slot ^ L::swz(row);
+      const int key = min(n0 + row, N - 1);  // rows past N: any valid row (masked later)
+      if (chunk < L::CPR) {
+        copy16_to_lds(Kh + (int64_t)key * D + 8 * chunk, stage + blk * 1024);
+        copy16_to_lds(Vh + (int64_t)key * D + 8 * chunk, stage + L::TILEB + blk * 1024);
+      }
+    }
+  };
+
+  // Per-lane LDS read offsets (bytes, relative to the stage).
+  const int krow = swap23(l32);  // S^T row -> key permutation (see key_of_reg)
+  int koff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * L::ROWB + 16 * ((2 * kk + h) ^ L::swz(krow));
+  const int g16 = lane >> 4;  // transpose reads work on 16-lane groups
+  const int dhalf = g16 & 1;
+  const int j16 = lane & 15;
+  int voff[2][DT];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int row = 8 * h + 4 * qq + (j16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int chunk = 4 * dt + 2 * dhalf + ((j16 & 3) >> 1);
+      voff[qq][dt] = L::TILEB + row * L::ROWB + 16 * (chunk ^ L::swz(row)) + 8 * (j16 & 1);
+    }
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  auto compute_tile = [&](int n0, const char* stage) {
+    if (n0 >= w_end) return;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const vec8 a0 = *reinterpret_cast<const vec8*>(stage + koff[kk]);
+      const vec8 a1 = *reinterpret_cast<const vec8*>(stage + koff[kk] + 32 * L::ROWB);
+      s[0] = T::mfma(a0, qreg[kk], s[0]);
+      s[1] = T::mfma(a1, qreg[kk], s[1]);
+    }
+    const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
+    if (need_mask) apply_mask<2>(s, n0, h, lim);
+    const float alpha = softmax_update<2>(s, c, m_run, l_run);
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      f32x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = s[cc >> 1][8 * (cc & 1) + e];
+      const vec8 pb = __builtin_convertvector(pf, vec8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(stage + voff[0][dt] + 16 * cc * L::ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(stage + voff[1][dt] + 16 * cc * L::ROWB));
+        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = T::mfma(a, pb, acc[dt]);
+      }
+    }
+  };
+
+  if (ntiles > 0) issue_tile(0, lds0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    // even tile: compute from lds0 while tile j+1 streams into lds1
+    if (j + 1 < ntiles) issue_tile((j + 1) * BN, lds1);
+    compute_tile(j * BN, lds0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    // odd tile: compute from lds1 while tile j+2 streams into lds0
+    if (j + 2 < ntiles) issue_tile((j + 2) * BN, lds0);
+    compute_tile((j + 1) * BN, lds1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qrow < M) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        elt y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (elt)(acc[dt][4 * g + e] * inv);
+        *reinterpret_cast<u32x2*>(Oh + (int64_t)qrow * D + d0) = __builtin_bit_cast(u32x2, y);
       }
     if (h == 0)
       Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
@@ -493,7 +701,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qrow < M) {
 #pragma unroll
@@ -529,6 +737,7 @@ struct Launch {
   float c;
   dim3 grid;
   hipStream_t stream;
+  bool generic;  // force the general kernel (register-staged tiles)
 };
 
 template <class T, int DP, bool CAUSAL>
@@ -557,8 +766,21 @@ void launch_f32(const Launch& a) {
                        (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c);
 }
 
+template <class T, int DP, bool CAUSAL>
+void launch_lp_fast(const Launch& a) {
+  using elt = typename T::elt;
+  hipLaunchKernelGGL((fa_fwd_lp_fast_kernel<T, DP, CAUSAL>), a.grid, dim3(NTHREADS), 0, a.stream,
+                     (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N,
+                     a.D, a.qtiles, a.c);
+}
+
 template <class T, bool CAUSAL>
 void dispatch_lp(const Launch& a) {
+  if (a.N > 0 && !a.generic) {
+    if (a.D == 128) return launch_lp_fast<T, 128, CAUSAL>(a);
+    if (a.D == 96) return launch_lp_fast<T, 96, CAUSAL>(a);
+    if (a.D == 64) return launch_lp_fast<T, 64, CAUSAL>(a);
+  }
   if (a.D <= 32) launch_lp<T, 32, CAUSAL>(a);
   else if (a.D <= 64) launch_lp<T, 64, CAUSAL>(a);
   else if (a.D <= 96) launch_lp<T, 96, CAUSAL>(a);
@@ -575,9 +797,9 @@ void dispatch_f32(const Launch& a) {
 
 }  // namespace
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
-                      int causal, int dtype, void* stream) {
+static int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                       int causal, int dtype, void* stream, bool generic) {
   const int st = fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (B == 0 || H == 0 || M == 0) return FA_OK;
@@ -595,6 +817,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   a.c = (float)((double)scale * 1.4426950408889634074);
   a.grid = dim3((unsigned)(B * H * a.qtiles));
   a.stream = (hipStream_t)stream;
+  a.generic = generic;
   (void)hipGetLastError();  // clear a stale error so the check below is about this launch
   switch (dtype) {
     case FA_DTYPE_F16:
@@ -608,4 +831,16 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
       break;
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                      int causal, int dtype, void* stream) {
+  return fa_fwd_impl(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream, false);
+}
+
+extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                              int causal, int dtype, void* stream) {
+  return fa_fwd_impl(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream, true);
 }

@@ -207,3 +207,26 @@ def test_deterministic_and_stream():
         o2, l2 = fa.fwd(qd, kd, vd, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fast_and_general_paths_agree(dtype, D, causal):
+    """fa_fwd's direct-to-LDS fast path against fa_fwd_general's register-staged
+    kernel: both match the oracle, and (same MFMA k-order, same softmax
+    arithmetic) they agree bit for bit."""
+    torch = _t()
+    M, N = (333, 517) if not causal else (517, 333)
+    _say(f"fast-vs-general dtype={dtype} D={D} causal={causal} M={M} N={N}")
+    q, k, v = _inputs(2, 2, M, N, D, dtype, 200 + D, q_mult=3.0)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    s = 1 / math.sqrt(D)
+    o1, l1 = fa.fwd(qd, kd, vd, causal=causal, scale=s)
+    o2, l2 = fa.fwd(qd, kd, vd, causal=causal, scale=s, general=True)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, s, causal)
+    check(f"fast_{dtype}_D{D}_c{int(causal)}", dtype, o1.double().cpu().numpy(), l1.cpu().numpy(), O_ref, L_ref)
+    check(f"general_{dtype}_D{D}_c{int(causal)}", dtype, o2.double().cpu().numpy(), l2.cpu().numpy(), O_ref, L_ref)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
