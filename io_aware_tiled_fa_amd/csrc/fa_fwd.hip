@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 
 namespace {
@@ -78,15 +80,27 @@ __device__ __forceinline__ int key_of_reg(int r, int h) {
   return 16 * (r >> 3) + 8 * h + (r & 7);
 }
 
-// Which workgroup works on which (batch*head, query tile).  Causal tiles are
-// issued heaviest first (the last query tile sees the most keys).
+// Which workgroup works on which (batch*head, query tile).
+// Workgroups are handed to the 8 XCDs round-robin (id % 8), and each XCD has
+// its own L2.  The id is remapped so that every XCD walks a contiguous range
+// of (head, query tile) pairs: the query tiles of one head then run on one XCD
+// at about the same time and share that head's K/V in its L2.  Within a head,
+// causal tiles are issued heaviest first (the last query tile sees the most
+// keys), so the light tiles fill the tail.
 struct TileCoord {
   int bh;
   int q0;
 };
+constexpr int NXCD = 8;
 template <bool CAUSAL>
 __device__ __forceinline__ TileCoord tile_coord(int qtiles) {
-  int t = blockIdx.x;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b % NXCD;
+  const int idx = b / NXCD;
+  const int per = G / NXCD;
+  const int rem = G % NXCD;
+  const int t = xcd * per + min(xcd, rem) + idx;  // contiguous range per XCD
   TileCoord c;
   c.bh = t / qtiles;
   int qt = t - c.bh * qtiles;
@@ -108,31 +122,54 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Row max and row sum over a lane's NT x 16 accumulator registers, as tree
+// reductions (short dependency chains; every kernel uses the same order).
+template <int NT>
+__device__ __forceinline__ float max_tree(const f32x16 (&s)[NT]) {
+  float m[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m[r] = s[0][r];
+#pragma unroll
+  for (int t = 1; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m[r] = fmaxf(m[r], s[t][r]);
+#pragma unroll
+  for (int wdt = 8; wdt >= 1; wdt >>= 1)
+#pragma unroll
+    for (int r = 0; r < wdt; ++r) m[r] = fmaxf(m[r], m[r + wdt]);
+  return m[0];
+}
+template <int NT>
+__device__ __forceinline__ float sum_tree(const f32x16 (&s)[NT]) {
+  float m[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m[r] = s[0][r];
+#pragma unroll
+  for (int t = 1; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m[r] = m[r] + s[t][r];
+#pragma unroll
+  for (int wdt = 8; wdt >= 1; wdt >>= 1)
+#pragma unroll
+    for (int r = 0; r < wdt; ++r) m[r] = m[r] + m[r + wdt];
+  return m[0];
+}
+
 // Online-softmax update for one lane's query row over NT accumulator tiles of
 // raw scores (already masked with -inf).  m_run is in scaled base-2 units.
 // Returns alpha, updates m_run / l_run, and replaces the scores with p.
 template <int NT>
 __device__ __forceinline__ float softmax_update(f32x16 (&s)[NT], float c, float& m_run,
                                                 float& l_run) {
-  float mx = s[0][0];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-  mx = pair_max(mx);
+  const float mx = pair_max(max_tree<NT>(s));
   const float m_new = fmaxf(m_run, mx * c);
   const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // all masked so far: clamp
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-  float sum = 0.0f;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_use));
-      s[t][r] = p;
-      sum += p;
-    }
-  l_run = l_run * alpha + sum;
+    for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_use));
+  l_run = l_run * alpha + sum_tree<NT>(s);
   m_run = m_new;
   return alpha;
 }
@@ -558,6 +595,216 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_fast_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Software-pipelined fast path (fp16/bf16, D in {64, 96, 128}).
+//
+// Per wave, tile j's softmax runs while the MFMA unit computes the scores of
+// tile j+1: S(j+1) = K(j+1) Q^T is issued first and its MFMAs are interleaved
+// with the VALU work of softmax(j) (max, exp2, sum, rounding P to 16 bits);
+// then O^T += V(j)^T P(j)^T.  K therefore runs one tile ahead of V, each with
+// its own pair of LDS buffers (same 64 KB as two K+V stages), and the copy
+// of K(j+2) and V(j+1) is in flight during step j.
+//
+template <class T, int DP, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
+    const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
+    const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
+    float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+  using elt = typename T::elt;
+  using vec8 = typename T::vec8;
+  using L = FastLayout<DP>;
+  constexpr int DT = DP / 32;
+  constexpr int KK = DP / 16;
+  constexpr int BPW = L::NBLK / 4;  // copy instructions per wave per tile matrix
+
+  __shared__ __attribute__((aligned(1024))) char kb0[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb1[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb0[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb1[L::TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<CAUSAL>(qtiles);
+  const int q0 = tc.q0;
+  const elt* Qh = q + (int64_t)tc.bh * M * D;
+  const elt* Kh = k + (int64_t)tc.bh * N * D;
+  const elt* Vh = v + (int64_t)tc.bh * N * D;
+  elt* Oh = o + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)tc.bh * M;
+
+  const int off = N - M;
+  const int qrow = q0 + 32 * w + l32;
+  const int wq_first = q0 + 32 * w;
+  const int wq_last = min(wq_first + 31, M - 1);
+  const int n_end = CAUSAL ? min(N, q0 + BM + off) : N;
+  const int ntiles = n_end > 0 ? (n_end + BN - 1) / BN : 0;
+  int w_end = CAUSAL ? min(N, wq_last + 1 + off) : N;
+  if (wq_first >= M) w_end = 0;
+  const int w_tiles = w_end > 0 ? (w_end + BN - 1) / BN : 0;  // tiles this wave computes
+  const int lim = CAUSAL ? min(N, qrow + off + 1) : N;
+
+  vec8 qreg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qrow < M) raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * kk + 8 * h);
+    qreg[kk] = __builtin_bit_cast(vec8, raw);
+  }
+
+  const int cp_sub = lane / L::SLOTS;
+  const int cp_slot = lane % L::SLOTS;
+  auto issue = [&](const elt* src, int n0, char* buf) {
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      const int blk = w * BPW + b;
+      const int row = blk * L::RPB + cp_sub;
+      const int chunk = cp_slot ^ L::swz(row);
+      const int key = min(n0 + row, N - 1);  // rows past N: any valid row (masked later)
+      if (chunk < L::CPR) copy16_to_lds(src + (int64_t)key * D + 8 * chunk, buf + blk * 1024);
+    }
+  };
+
+  const int krow = swap23(l32);
+  int koff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * L::ROWB + 16 * ((2 * kk + h) ^ L::swz(krow));
+  const int g16 = lane >> 4;
+  const int dhalf = g16 & 1;
+  const int j16 = lane & 15;
+  int voff[2][DT];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int row = 8 * h + 4 * qq + (j16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int chunk = 4 * dt + 2 * dhalf + ((j16 & 3) >> 1);
+      voff[qq][dt] = row * L::ROWB + 16 * (chunk ^ L::swz(row)) + 8 * (j16 & 1);
+    }
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  auto s_mfma = [&](f32x16 (&sx)[2], const char* kbuf) {
+    sx[0] = f32x16{};
+    sx[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const vec8 a0 = *reinterpret_cast<const vec8*>(kbuf + koff[kk]);
+      const vec8 a1 = *reinterpret_cast<const vec8*>(kbuf + koff[kk] + 32 * L::ROWB);
+      sx[0] = T::mfma(a0, qreg[kk], sx[0]);
+      sx[1] = T::mfma(a1, qreg[kk], sx[1]);
+    }
+  };
+
+  // One step of a wave: softmax(cur) and O += V^T P^T for tile n0, with the
+  // scores of the next tile (into nxt) computed underneath when NEXT.
+  auto body = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[2], f32x16 (&nxt)[2],
+                  const char* kbuf_next, const char* vbuf, int n0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    if (NEXT) s_mfma(nxt, kbuf_next);
+    if (MASK) apply_mask<2>(cur, n0, h, lim);
+    const float alpha = softmax_update<2>(cur, c, m_run, l_run);
+    vec8 pb[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      f32x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = cur[cc >> 1][8 * (cc & 1) + e];
+      pb[cc] = __builtin_convertvector(pf, vec8);
+    }
+    if (NEXT) {
+      // interleave: each S MFMA of the next tile with a slice of the softmax VALU work
+#pragma unroll
+      for (int i = 0; i < 2 * KK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+      }
+    }
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vbuf + voff[0][dt] + 16 * cc * L::ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vbuf + voff[1][dt] + 16 * cc * L::ROWB));
+        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = T::mfma(a, pb[cc], acc[dt]);
+      }
+    }
+  };
+
+  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const char* kbuf_next,
+                  const char* vbuf, char* kbuf_load, char* vbuf_load) {
+    if (j + 2 < ntiles) issue(Kh, (j + 2) * BN, kbuf_load);
+    if (j + 1 < ntiles) issue(Vh, (j + 1) * BN, vbuf_load);
+    if (j < w_tiles) {
+      const int n0 = j * BN;
+      const bool next = j + 1 < w_tiles;
+      const bool mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
+      using T0 = std::integral_constant<bool, false>;
+      using T1 = std::integral_constant<bool, true>;
+      if (!mask) {
+        if (next) body(T0{}, T1{}, cur, nxt, kbuf_next, vbuf, n0);
+        else body(T0{}, T0{}, cur, nxt, kbuf_next, vbuf, n0);
+      } else {
+        if (next) body(T1{}, T1{}, cur, nxt, kbuf_next, vbuf, n0);
+        else body(T1{}, T0{}, cur, nxt, kbuf_next, vbuf, n0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  f32x16 sa[2], sb[2];
+  if (ntiles > 0) {
+    issue(Kh, 0, kb0);
+    issue(Vh, 0, vb0);
+  }
+  if (ntiles > 1) issue(Kh, BN, kb1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (0 < w_tiles) s_mfma(sa, kb0);
+  __syncthreads();  // every wave is done reading K(0) before K(2) overwrites it
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, sa, sb, kb1, vb0, kb0, vb1);
+    if (j + 1 >= ntiles) break;
+    step(j + 1, sb, sa, kb0, vb1, kb1, vb0);
+  }
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qrow < M) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        elt y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (elt)(acc[dt][4 * g + e] * inv);
+        *reinterpret_cast<u32x2*>(Oh + (int64_t)qrow * D + d0) = __builtin_bit_cast(u32x2, y);
+      }
+    if (h == 0)
+      Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 kernel: same structure on v_mfma_f32_32x32x2f32 with P kept in fp32.
 // 32-key tiles; K rows in LDS at an odd stride (conflict-free column reads),
@@ -769,7 +1016,7 @@ void launch_f32(const Launch& a) {
 template <class T, int DP, bool CAUSAL>
 void launch_lp_fast(const Launch& a) {
   using elt = typename T::elt;
-  hipLaunchKernelGGL((fa_fwd_lp_fast_kernel<T, DP, CAUSAL>), a.grid, dim3(NTHREADS), 0, a.stream,
+  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, CAUSAL>), a.grid, dim3(NTHREADS), 0, a.stream,
                      (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N,
                      a.D, a.qtiles, a.c);
 }
