@@ -108,12 +108,15 @@ def main():
     ap.add_argument("--workload", default=BENCH_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of attention, run a plain device-to-device copy of BYTES "
+                         "(3 times); used to scale the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the attention forward path here has no "
-              "multi-GPU mode (each (batch, head) is independent; see the sharding notes in "
-              "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: every (batch, head) of the attention forward "
+              "pass is independent, so a multi-GPU run would shard heads with no communication, "
+              "and this benchmark reports the one-GPU share. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -123,6 +126,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {4 * n} bytes 3 times")
+        return
     fa.load()
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

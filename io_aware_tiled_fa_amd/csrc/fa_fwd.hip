@@ -157,21 +157,40 @@ __device__ __forceinline__ float sum_tree(const f32x16 (&s)[NT]) {
 
 // Online-softmax update for one lane's query row over NT accumulator tiles of
 // raw scores (already masked with -inf).  m_run is in scaled base-2 units.
-// Returns alpha, updates m_run / l_run, and replaces the scores with p.
+//
+// The reference maximum moves lazily: only when the tile's row max exceeds it
+// by more than RESCALE_TAU (base-2 units).  Until then p = exp2(s*c - m_run)
+// may reach 2^RESCALE_TAU, far inside fp32 / fp16 / bf16 range, and because
+// l and the accumulator share the same reference the final acc / l and
+// LSE = m_run + log2(l) are the same numbers (only the rounding differs).  In
+// exchange the O rescale and its 64 multiplies per tile disappear once a
+// row's max has settled, which is most tiles.  The first visible tile of a row
+// always sets the reference (m_run = -inf before it).
+//
+// Returns alpha (1 where the reference did not move) and whether any lane of
+// the wave moved a finite reference (then O must be rescaled).  Replaces the
+// scores with p and updates m_run / l_run.
+constexpr float RESCALE_TAU = 8.0f;
+struct SoftmaxStep {
+  float alpha;
+  bool rescale;
+};
 template <int NT>
-__device__ __forceinline__ float softmax_update(f32x16 (&s)[NT], float c, float& m_run,
-                                                float& l_run) {
-  const float mx = pair_max(max_tree<NT>(s));
-  const float m_new = fmaxf(m_run, mx * c);
-  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // all masked so far: clamp
+__device__ __forceinline__ SoftmaxStep softmax_update(f32x16 (&s)[NT], float c, float& m_run,
+                                                      float& l_run) {
+  const float mx = pair_max(max_tree<NT>(s)) * c;
+  const bool move = mx > m_run + RESCALE_TAU;  // also true for the first visible tile
+  const float m_new = move ? mx : m_run;
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // nothing visible yet: clamp
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_use));
   l_run = l_run * alpha + sum_tree<NT>(s);
+  const bool rescale = __any(move && m_run != -INFINITY);
   m_run = m_new;
-  return alpha;
+  return SoftmaxStep{alpha, rescale};
 }
 
 // Mask keys a lane's row may not see in the tile starting at key n0.
@@ -354,9 +373,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
       }
       const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
       if (need_mask) apply_mask<2>(s, n0, h, lim);
-      const float alpha = softmax_update<2>(s, c, m_run, l_run);
+      const SoftmaxStep st = softmax_update<2>(s, c, m_run, l_run);
+      if (st.rescale) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= st.alpha;
+      }
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         f32x8 pf;
@@ -434,167 +455,6 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, char* lds_block) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
                                    (void __attribute__((address_space(3)))*)lds_block, 16, 0, 0);
 }
-
-template <class T, int DP, bool CAUSAL>
-__global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_fast_kernel(
-    const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
-    const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
-    float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
-  using elt = typename T::elt;
-  using vec8 = typename T::vec8;
-  using L = FastLayout<DP>;
-  constexpr int DT = DP / 32;
-  constexpr int KK = DP / 16;
-  constexpr int BPW = L::NBLK / 4;  // copy instructions per wave per tile matrix
-
-  __shared__ __attribute__((aligned(1024))) char lds0[L::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char lds1[L::STAGEB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-
-  const TileCoord tc = tile_coord<CAUSAL>(qtiles);
-  const int q0 = tc.q0;
-  const elt* Qh = q + (int64_t)tc.bh * M * D;
-  const elt* Kh = k + (int64_t)tc.bh * N * D;
-  const elt* Vh = v + (int64_t)tc.bh * N * D;
-  elt* Oh = o + (int64_t)tc.bh * M * D;
-  float* Lh = lse + (int64_t)tc.bh * M;
-
-  const int off = N - M;
-  const int qrow = q0 + 32 * w + l32;
-  const int wq_first = q0 + 32 * w;
-  const int wq_last = min(wq_first + 31, M - 1);
-  const int n_end = CAUSAL ? min(N, q0 + BM + off) : N;
-  const int ntiles = n_end > 0 ? (n_end + BN - 1) / BN : 0;
-  int w_end = CAUSAL ? min(N, wq_last + 1 + off) : N;
-  if (wq_first >= M) w_end = 0;
-  const int lim = CAUSAL ? min(N, qrow + off + 1) : N;
-
-  vec8 qreg[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qrow < M) raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * kk + 8 * h);
-    qreg[kk] = __builtin_bit_cast(vec8, raw);
-  }
-
-  // Per-lane copy plan: slot `lane` of each 1 KB block holds logical chunk
-  // (lane % SLOTS) ^ swz(row) of row (blk * RPB + lane / SLOTS).
-  const int cp_sub = lane / L::SLOTS;
-  const int cp_slot = lane % L::SLOTS;
-  auto issue_tile = [&](int n0, char* stage) {
-#pragma unroll
-    for (int b = 0; b < BPW; ++b) {
-      const int blk = w * BPW + b;
-      const int row = blk * L::RPB + cp_sub;
-      const int chunk = cp_slot ^ L::swz(row);
-      const int key = min(n0 + row, N - 1);  // rows past N: any valid row (masked later)
-      if (chunk < L::CPR) {
-        copy16_to_lds(Kh + (int64_t)key * D + 8 * chunk, stage + blk * 1024);
-        copy16_to_lds(Vh + (int64_t)key * D + 8 * chunk, stage + L::TILEB + blk * 1024);
-      }
-    }
-  };
-
-  // Per-lane LDS read offsets (bytes, relative to the stage).
-  const int krow = swap23(l32);  // S^T row -> key permutation (see key_of_reg)
-  int koff[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * L::ROWB + 16 * ((2 * kk + h) ^ L::swz(krow));
-  const int g16 = lane >> 4;  // transpose reads work on 16-lane groups
-  const int dhalf = g16 & 1;
-  const int j16 = lane & 15;
-  int voff[2][DT];
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const int row = 8 * h + 4 * qq + (j16 >> 2);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int chunk = 4 * dt + 2 * dhalf + ((j16 & 3) >> 1);
-      voff[qq][dt] = L::TILEB + row * L::ROWB + 16 * (chunk ^ L::swz(row)) + 8 * (j16 & 1);
-    }
-  }
-
-  f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-
-  auto compute_tile = [&](int n0, const char* stage) {
-    if (n0 >= w_end) return;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const vec8 a0 = *reinterpret_cast<const vec8*>(stage + koff[kk]);
-      const vec8 a1 = *reinterpret_cast<const vec8*>(stage + koff[kk] + 32 * L::ROWB);
-      s[0] = T::mfma(a0, qreg[kk], s[0]);
-      s[1] = T::mfma(a1, qreg[kk], s[1]);
-    }
-    const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
-    if (need_mask) apply_mask<2>(s, n0, h, lim);
-    const float alpha = softmax_update<2>(s, c, m_run, l_run);
-    if (!__all(alpha == 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-    }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      f32x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = s[cc >> 1][8 * (cc & 1) + e];
-      const vec8 pb = __builtin_convertvector(pf, vec8);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(stage + voff[0][dt] + 16 * cc * L::ROWB));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(stage + voff[1][dt] + 16 * cc * L::ROWB));
-        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[dt] = T::mfma(a, pb, acc[dt]);
-      }
-    }
-  };
-
-  if (ntiles > 0) issue_tile(0, lds0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    // even tile: compute from lds0 while tile j+1 streams into lds1
-    if (j + 1 < ntiles) issue_tile((j + 1) * BN, lds1);
-    compute_tile(j * BN, lds0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 >= ntiles) break;
-    // odd tile: compute from lds1 while tile j+2 streams into lds0
-    if (j + 2 < ntiles) issue_tile((j + 2) * BN, lds0);
-    compute_tile((j + 1) * BN, lds1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qrow < M) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * h;
-        elt y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (elt)(acc[dt][4 * g + e] * inv);
-        *reinterpret_cast<u32x2*>(Oh + (int64_t)qrow * D + d0) = __builtin_bit_cast(u32x2, y);
-      }
-    if (h == 0)
-      Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
-  }
-}
-
 
 // ---------------------------------------------------------------------------
 // Software-pipelined fast path (fp16/bf16, D in {64, 96, 128}).
@@ -713,7 +573,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
     constexpr bool NEXT = decltype(next_tag)::value;
     if (NEXT) s_mfma(nxt, kbuf_next);
     if (MASK) apply_mask<2>(cur, n0, h, lim);
-    const float alpha = softmax_update<2>(cur, c, m_run, l_run);
+    const SoftmaxStep st = softmax_update<2>(cur, c, m_run, l_run);
     vec8 pb[4];
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -723,17 +583,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
       pb[cc] = __builtin_convertvector(pf, vec8);
     }
     if (NEXT) {
-      // interleave: each S MFMA of the next tile with a slice of the softmax VALU work
+      // Interleave each score MFMA of the next tile with a slice of the softmax
+      // VALU work; K operand reads run four MFMAs ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
 #pragma unroll
       for (int i = 0; i < 2 * KK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // 10 VALU
+        if (i < 2 * KK - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read
       }
     }
-    if (!__all(alpha == 1.0f)) {
+    if (st.rescale) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= st.alpha;
     }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -746,6 +608,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
         const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = T::mfma(a, pb[cc], acc[dt]);
       }
+    }
+    // V^T operand reads run two MFMAs ahead of the PV MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (i < 4 * DT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
   };
 
@@ -932,9 +801,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
                                                     0, 0, 0);
       const bool need_mask = (n0 + BN32 > N) || (CAUSAL && n0 + BN32 - 1 > wq_first + off);
       if (need_mask) apply_mask<1>(s, n0, h, lim);
-      const float alpha = softmax_update<1>(s, c, m_run, l_run);
+      const SoftmaxStep st = softmax_update<1>(s, c, m_run, l_run);
+      if (st.rescale) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= st.alpha;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key_of_reg(r, h);
