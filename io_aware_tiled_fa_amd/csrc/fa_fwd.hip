@@ -124,20 +124,34 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // Row max and row sum over a lane's NT x 16 accumulator registers, as tree
 // reductions (short dependency chains; every kernel uses the same order).
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Row max with three-input maxima (v_max3_f32), fixed order.
+__device__ __forceinline__ float max_tree16(const f32x16& s) {
+  const float a0 = fmax3(s[0], s[1], s[2]), a1 = fmax3(s[3], s[4], s[5]);
+  const float a2 = fmax3(s[6], s[7], s[8]), a3 = fmax3(s[9], s[10], s[11]);
+  const float a4 = fmax3(s[12], s[13], s[14]);
+  return fmaxf(fmax3(a0, a1, a2), fmax3(a3, a4, s[15]));
+}
 template <int NT>
-__device__ __forceinline__ float max_tree(const f32x16 (&s)[NT]) {
-  float m[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) m[r] = s[0][r];
-#pragma unroll
-  for (int t = 1; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m[r] = fmaxf(m[r], s[t][r]);
-#pragma unroll
-  for (int wdt = 8; wdt >= 1; wdt >>= 1)
-#pragma unroll
-    for (int r = 0; r < wdt; ++r) m[r] = fmaxf(m[r], m[r + wdt]);
-  return m[0];
+__device__ __forceinline__ float max_tree(const f32x16 (&s)[NT]);
+template <>
+__device__ __forceinline__ float max_tree<1>(const f32x16 (&s)[1]) {
+  return max_tree16(s[0]);
+}
+template <>
+__device__ __forceinline__ float max_tree<2>(const f32x16 (&s)[2]) {
+  const f32x16& x = s[0];
+  const f32x16& y = s[1];
+  const float a0 = fmax3(x[0], x[1], x[2]), a1 = fmax3(x[3], x[4], x[5]);
+  const float a2 = fmax3(x[6], x[7], x[8]), a3 = fmax3(x[9], x[10], x[11]);
+  const float a4 = fmax3(x[12], x[13], x[14]), a5 = fmax3(x[15], y[0], y[1]);
+  const float a6 = fmax3(y[2], y[3], y[4]), a7 = fmax3(y[5], y[6], y[7]);
+  const float a8 = fmax3(y[8], y[9], y[10]), a9 = fmax3(y[11], y[12], y[13]);
+  const float a10 = fmaxf(y[14], y[15]);
+  const float b0 = fmax3(a0, a1, a2), b1 = fmax3(a3, a4, a5), b2 = fmax3(a6, a7, a8);
+  const float b3 = fmaxf(a9, a10);
+  return fmaxf(fmax3(b0, b1, b2), b3);
 }
 template <int NT>
 __device__ __forceinline__ float sum_tree(const f32x16 (&s)[NT]) {
@@ -439,12 +453,17 @@ struct FastLayout {
   static constexpr int CPR = DP / 8;                  // 16-byte chunks holding data
   static constexpr int SLOTS = ROWB / 16;             // 16-byte slots per row
   static constexpr int TILEB = BN * ROWB;             // one K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
   static constexpr int RPB = 1024 / ROWB;             // rows per 1 KB copy instruction
   static constexpr int NBLK = TILEB / 1024;           // copy instructions per tile matrix
-  // physical slot of logical chunk c in row r is c ^ swz(r)
-  static __device__ __forceinline__ int swz(int r) {
+  // Physical slot of logical chunk c in row r is c ^ swz(r).
+  // K: the 16 rows of a score-MFMA read land on 16 distinct slots.
+  static __device__ __forceinline__ int swz_k(int r) {
     return DP == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+  }
+  // V: the 4 rows of a transpose read land in 4 distinct 64-byte bank groups;
+  // depends only on r mod 4 so that rows 4 apart share the pattern.
+  static __device__ __forceinline__ int swz_v(int r) {
+    return DP == 64 ? (((r >> 1) & 1) << 2) : ((r & 3) << 2);
   }
 };
 
@@ -466,11 +485,17 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, char* lds_block) {
 // its own pair of LDS buffers (same 64 KB as two K+V stages), and the copy
 // of K(j+2) and V(j+1) is in flight during step j.
 //
-template <class T, int DP, bool CAUSAL>
+// One instantiation serves causal and non-causal calls: `off` is the causal
+// diagonal offset (key j visible to row i iff j <= i + off), N - M for a
+// bottom-right causal mask and N for no mask (no row can reach it, so only the
+// N tail is ever masked).
+template <class T, int DP>
 __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
-    float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+    float* __restrict__ lse, int M, int N, int off, int qtiles, float c) {
+  constexpr bool CAUSAL = true;  // masking logic always on; `off` decides what it masks
+  constexpr int D = DP;          // the dispatcher routes only D == DP here
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using L = FastLayout<DP>;
@@ -497,7 +522,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
   elt* Oh = o + (int64_t)tc.bh * M * D;
   float* Lh = lse + (int64_t)tc.bh * M;
 
-  const int off = N - M;
   const int qrow = q0 + 32 * w + l32;
   const int wq_first = q0 + 32 * w;
   const int wq_last = min(wq_first + 31, M - 1);
@@ -518,32 +542,55 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
 
   const int cp_sub = lane / L::SLOTS;
   const int cp_slot = lane % L::SLOTS;
-  auto issue = [&](const elt* src, int n0, char* buf) {
+  // Copy plan: wave w issues the 1 KB copy instructions i = w + 4b (b < BPW).
+  // Instruction i fills LDS rows i*RPB .. i*RPB+RPB-1; lane l writes slot
+  // l % SLOTS of row i*RPB + l / SLOTS.  Because 4*RPB rows span a whole period
+  // of both swizzles, the logical chunk a lane copies does not depend on b, and
+  // one byte offset per matrix serves all of the lane's copies (b only adds
+  // 4*RPB rows).
+  const int cp_row = w * L::RPB + cp_sub;  // row of the lane's first copy (b = 0)
+  const int chunk_k = cp_slot ^ L::swz_k(cp_row);
+  const int chunk_v = cp_slot ^ L::swz_v(cp_row);
+  const unsigned goff_k = (unsigned)((cp_row * D + 8 * chunk_k) * (int)sizeof(elt));
+  const unsigned goff_v = (unsigned)((cp_row * D + 8 * chunk_v) * (int)sizeof(elt));
+  constexpr int BSTEP = 4 * L::RPB;  // rows between a lane's consecutive copies
+  const int lds_w = __builtin_amdgcn_readfirstlane(w * 1024);  // wave-uniform LDS offset
+  auto issue = [&](const elt* src, int n0, char* buf, bool is_v) {
+    const int chunk = is_v ? chunk_v : chunk_k;
+    if (chunk >= L::CPR) return;  // D = 96: slots 12..15 of a row hold no data
+    const unsigned goff = is_v ? goff_v : goff_k;
+    if (n0 + BN <= N) {
+      const char* base = reinterpret_cast<const char*>(src + (int64_t)n0 * D);
 #pragma unroll
-    for (int b = 0; b < BPW; ++b) {
-      const int blk = w * BPW + b;
-      const int row = blk * L::RPB + cp_sub;
-      const int chunk = cp_slot ^ L::swz(row);
-      const int key = min(n0 + row, N - 1);  // rows past N: any valid row (masked later)
-      if (chunk < L::CPR) copy16_to_lds(src + (int64_t)key * D + 8 * chunk, buf + blk * 1024);
+      for (int b = 0; b < BPW; ++b)
+        copy16_to_lds(base + goff + (unsigned)(b * BSTEP * D * (int)sizeof(elt)),
+                      buf + lds_w + 4096 * b);
+    } else {  // N tail: rows past N copy row N-1 instead (their scores are masked)
+#pragma unroll
+      for (int b = 0; b < BPW; ++b) {
+        const int key = min(n0 + cp_row + b * BSTEP, N - 1);
+        copy16_to_lds(src + (int64_t)key * D + 8 * chunk, buf + lds_w + 4096 * b);
+      }
     }
   };
 
   const int krow = swap23(l32);
   int koff[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * L::ROWB + 16 * ((2 * kk + h) ^ L::swz(krow));
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * L::ROWB + 16 * ((2 * kk + h) ^ L::swz_k(krow));
+  // V^T transpose reads: lane j of a 16-lane group addresses row (8h + 4q + j/4)
+  // of the 16-key chunk and 4 columns starting at 32dt + 16*dhalf + 4*(j%4).
+  // Rows 4 apart share the swizzle, so q (and the key chunk) are immediates.
   const int g16 = lane >> 4;
   const int dhalf = g16 & 1;
   const int j16 = lane & 15;
-  int voff[2][DT];
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const int row = 8 * h + 4 * qq + (j16 >> 2);
+  int voff[DT];
+  {
+    const int row = 8 * h + (j16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int chunk = 4 * dt + 2 * dhalf + ((j16 & 3) >> 1);
-      voff[qq][dt] = row * L::ROWB + 16 * (chunk ^ L::swz(row)) + 8 * (j16 & 1);
+      voff[dt] = row * L::ROWB + 16 * (chunk ^ L::swz_v(row)) + 8 * (j16 & 1);
     }
   }
 
@@ -602,9 +649,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vbuf + voff[0][dt] + 16 * cc * L::ROWB));
+            (lds_i16x4*)(vbuf + voff[dt] + 16 * cc * L::ROWB));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vbuf + voff[1][dt] + 16 * cc * L::ROWB));
+            (lds_i16x4*)(vbuf + voff[dt] + (16 * cc + 4) * L::ROWB));
         const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = T::mfma(a, pb[cc], acc[dt]);
       }
@@ -620,8 +667,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
 
   auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const char* kbuf_next,
                   const char* vbuf, char* kbuf_load, char* vbuf_load) {
-    if (j + 2 < ntiles) issue(Kh, (j + 2) * BN, kbuf_load);
-    if (j + 1 < ntiles) issue(Vh, (j + 1) * BN, vbuf_load);
+    if (j + 2 < ntiles) issue(Kh, (j + 2) * BN, kbuf_load, false);
+    if (j + 1 < ntiles) issue(Vh, (j + 1) * BN, vbuf_load, true);
     if (j < w_tiles) {
       const int n0 = j * BN;
       const bool next = j + 1 < w_tiles;
@@ -642,10 +689,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
 
   f32x16 sa[2], sb[2];
   if (ntiles > 0) {
-    issue(Kh, 0, kb0);
-    issue(Vh, 0, vb0);
+    issue(Kh, 0, kb0, false);
+    issue(Vh, 0, vb0, true);
   }
-  if (ntiles > 1) issue(Kh, BN, kb1);
+  if (ntiles > 1) issue(Kh, BN, kb1, false);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (0 < w_tiles) s_mfma(sa, kb0);
@@ -887,9 +934,10 @@ void launch_f32(const Launch& a) {
 template <class T, int DP, bool CAUSAL>
 void launch_lp_fast(const Launch& a) {
   using elt = typename T::elt;
-  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, CAUSAL>), a.grid, dim3(NTHREADS), 0, a.stream,
+  const int off = CAUSAL ? a.N - a.M : a.N;
+  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP>), a.grid, dim3(NTHREADS), 0, a.stream,
                      (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N,
-                     a.D, a.qtiles, a.c);
+                     off, a.qtiles, a.c);
 }
 
 template <class T, bool CAUSAL>
