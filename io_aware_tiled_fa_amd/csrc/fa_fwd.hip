@@ -170,21 +170,13 @@ __device__ __forceinline__ float sum_tree(const f32x16 (&s)[NT]) {
 }
 
 // Online-softmax update for one lane's query row over NT accumulator tiles of
-// raw scores (already masked with -inf).  m_run is in scaled base-2 units.
-//
-// The reference maximum moves lazily: only when the tile's row max exceeds it
-// by more than RESCALE_TAU (base-2 units).  Until then p = exp2(s*c - m_run)
-// may reach 2^RESCALE_TAU, far inside fp32 / fp16 / bf16 range, and because
-// l and the accumulator share the same reference the final acc / l and
-// LSE = m_run + log2(l) are the same numbers (only the rounding differs).  In
-// exchange the O rescale and its 64 multiplies per tile disappear once a
-// row's max has settled, which is most tiles.  The first visible tile of a row
-// always sets the reference (m_run = -inf before it).
-//
-// Returns alpha (1 where the reference did not move) and whether any lane of
-// the wave moved a finite reference (then O must be rescaled).  Replaces the
-// scores with p and updates m_run / l_run.
-constexpr float RESCALE_TAU = 8.0f;
+// raw scores (already masked with -inf).  m_run is in scaled base-2 units:
+//   m_new = max(m_run, rowmax * c),  alpha = exp2(m_run - m_new),
+//   p = exp2(s * c - m_new),         l_run = l_run * alpha + sum(p).
+// An all-masked running max (-inf) is clamped to 0 before it is subtracted.
+// Replaces the scores with p.  Returns alpha and whether any lane of the wave
+// moved a finite maximum (otherwise alpha is 1 everywhere and the O rescale is
+// skipped; multiplying by 1 would change nothing).
 struct SoftmaxStep {
   float alpha;
   bool rescale;
@@ -193,8 +185,7 @@ template <int NT>
 __device__ __forceinline__ SoftmaxStep softmax_update(f32x16 (&s)[NT], float c, float& m_run,
                                                       float& l_run) {
   const float mx = pair_max(max_tree<NT>(s)) * c;
-  const bool move = mx > m_run + RESCALE_TAU;  // also true for the first visible tile
-  const float m_new = move ? mx : m_run;
+  const float m_new = fmaxf(m_run, mx);
   const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // nothing visible yet: clamp
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
 #pragma unroll
@@ -202,9 +193,22 @@ __device__ __forceinline__ SoftmaxStep softmax_update(f32x16 (&s)[NT], float c, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_use));
   l_run = l_run * alpha + sum_tree<NT>(s);
-  const bool rescale = __any(move && m_run != -INFINITY);
+  const bool rescale = __any(m_new > m_run && m_run != -INFINITY);
   m_run = m_new;
   return SoftmaxStep{alpha, rescale};
+}
+
+// p of a 64-key tile rounded to the 16-bit input type: pb[cc] holds keys
+// 16cc + 8h + e (e = 0..7), the B operand of the PV MFMA for key chunk cc.
+template <class T>
+__device__ __forceinline__ void pack_p(const f32x16 (&s)[2], typename T::vec8 (&pb)[4]) {
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    f32x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = s[cc >> 1][8 * (cc & 1) + e];
+    pb[cc] = __builtin_convertvector(pf, typename T::vec8);
+  }
 }
 
 // Mask keys a lane's row may not see in the tile starting at key n0.
@@ -388,21 +392,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
       const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
       if (need_mask) apply_mask<2>(s, n0, h, lim);
       const SoftmaxStep st = softmax_update<2>(s, c, m_run, l_run);
+      vec8 pb[4];
+      pack_p<T>(s, pb);
       if (st.rescale) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt] *= st.alpha;
       }
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        f32x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = s[cc >> 1][8 * (cc & 1) + e];
-        const vec8 pb = __builtin_convertvector(pf, vec8);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const vec8 a =
               *reinterpret_cast<const vec8*>(Vs + (32 * dt + l32) * VSTR + 16 * cc + 8 * h);
-          acc[dt] = T::mfma(a, pb, acc[dt]);
+          acc[dt] = T::mfma(a, pb[cc], acc[dt]);
         }
       }
     }
@@ -622,13 +624,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
     if (MASK) apply_mask<2>(cur, n0, h, lim);
     const SoftmaxStep st = softmax_update<2>(cur, c, m_run, l_run);
     vec8 pb[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      f32x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = cur[cc >> 1][8 * (cc & 1) + e];
-      pb[cc] = __builtin_convertvector(pf, vec8);
-    }
+    pack_p<T>(cur, pb);
     if (NEXT) {
       // Interleave each score MFMA of the next tile with a slice of the softmax
       // VALU work; K operand reads run four MFMAs ahead.

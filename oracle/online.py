@@ -39,13 +39,6 @@ Failure modes the pages name, available as switches for negative-control tests:
 * ``sentinel=-1e6``: masking with a finite sentinel instead of -inf ("Causal
   masking": the sentinel becomes the max and inflates the running sum).
 * ``reverse=True``: visit K/V blocks last-to-first (Module 08 "Practice" 2).
-
-``lazy_tau`` models a variant the HIP kernel uses: the running reference max
-moves only when a tile's row max exceeds it by more than ``lazy_tau`` (in the
-exponent's base); until then p may exceed 1 (by at most 2**lazy_tau in base
-two).  l and acc share the reference, so acc / l and m + log(l) are the same
-quantities; ``tests/test_oracle_negative_controls.py`` checks it against the
-definition.
 """
 
 from __future__ import annotations
@@ -94,8 +87,7 @@ def tiled_attention(q, k, v, scale: float, causal: bool = False,
                     base2: bool = True, rescale: bool = True,
                     alpha_base_e: bool = False, guard: bool = True,
                     sentinel: float | None = None, reverse: bool = False,
-                    skip_masked_tiles: bool = True, history: list | None = None,
-                    lazy_tau: float | None = None):
+                    skip_masked_tiles: bool = True, history: list | None = None):
     """Tiled exact attention for one head by the online recurrence (fp64).
 
     q: [M, D], k: [N, D], v: [N, Dv].  Returns (O, LSE, m, l) where m is in the
@@ -138,11 +130,7 @@ def tiled_attention(q, k, v, scale: float, causal: bool = False,
             if causal:
                 vis = cols[None, :] <= rows[:, None] + (N - M)
                 t = np.where(vis, t, mask_value)
-            if lazy_tau is None:
-                m_new = np.maximum(m, t.max(axis=1))
-            else:  # move the reference only when the row max clears it by lazy_tau
-                tmax = t.max(axis=1)
-                m_new = np.where(tmax > m + lazy_tau, tmax, m)
+            m_new = np.maximum(m, t.max(axis=1))
             m_use = np.where(np.isneginf(m_new), 0.0, m_new) if guard else m_new
             with np.errstate(invalid="ignore", over="ignore"):
                 alpha = ex_alpha(m - m_use)
