@@ -45,7 +45,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, qc, kc, vc, budget_s: float = 15.0, max_heads: int = 32):
+def cpu_baseline(w, qc, kc, vc, budget_s: float = 15.0, max_heads: int = 1 << 30):
     """Time the fp64 oracle on whole heads of the workload until ~budget_s."""
     import numpy as np
 
@@ -214,7 +214,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": "fa_fwd_lp_kernel" if w.dtype != "f32" else "fa_fwd_f32_kernel",
+            "kernel": ("fa_fwd_f32_kernel" if w.dtype == "f32" else
+                       "fa_fwd_lp_pipe_kernel" if w.D in (64, 96, 128) else "fa_fwd_lp_kernel"),
             "avg_launch_ms": round(avg_launch_ms, 5),
             "hbm_gbs_compulsory": round(compulsory_bytes(w) / (avg_launch_ms * 1e-3) / 1e9, 1),
         },
