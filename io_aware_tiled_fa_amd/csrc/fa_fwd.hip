@@ -92,7 +92,7 @@ struct TileCoord {
   int q0;
 };
 constexpr int NXCD = 8;
-template <bool CAUSAL>
+template <bool CAUSAL, int ROWS = BM>
 __device__ __forceinline__ TileCoord tile_coord(int qtiles) {
   const int G = gridDim.x;
   const int b = blockIdx.x;
@@ -105,7 +105,7 @@ __device__ __forceinline__ TileCoord tile_coord(int qtiles) {
   c.bh = t / qtiles;
   int qt = t - c.bh * qtiles;
   if (CAUSAL) qt = qtiles - 1 - qt;
-  c.q0 = qt * BM;
+  c.q0 = qt * ROWS;
   return c;
 }
 
@@ -213,14 +213,17 @@ __device__ __forceinline__ void pack_p(const f32x16 (&s)[2], typename T::vec8 (&
 
 // Mask keys a lane's row may not see in the tile starting at key n0.
 // lim: exclusive key limit of the row (min(N, i + N - M + 1) or N).
+// The test key >= lim is done as (key - n0 - 8h) >= (lim - n0 - 8h): the left
+// side is a compile-time constant per register, so the mask needs one
+// per-lane threshold instead of a key offset per register.
 template <int NT>
 __device__ __forceinline__ void apply_mask(f32x16 (&s)[NT], int n0, int h, int lim) {
+  const int thr = lim - n0 - 8 * h;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = n0 + 32 * t + key_of_reg(r, h);
-      if (key >= lim) s[t][r] = -INFINITY;
+      if (32 * t + key_of_reg(r, 0) >= thr) s[t][r] = -INFINITY;
     }
 }
 
@@ -491,8 +494,8 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, char* lds_block) {
 // diagonal offset (key j visible to row i iff j <= i + off), N - M for a
 // bottom-right causal mask and N for no mask (no row can reach it, so only the
 // N tail is ever masked).
-template <class T, int DP>
-__global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
+template <class T, int DP, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
     float* __restrict__ lse, int M, int N, int off, int qtiles, float c) {
@@ -503,7 +506,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
   using L = FastLayout<DP>;
   constexpr int DT = DP / 32;
   constexpr int KK = DP / 16;
-  constexpr int BPW = L::NBLK / 4;  // copy instructions per wave per tile matrix
+  constexpr int BPW = L::NBLK / NW;  // copy instructions per wave per tile matrix
+  constexpr int ROWS = 32 * NW;      // query rows per workgroup
+  static_assert(L::NBLK % NW == 0, "copy plan");
 
   __shared__ __attribute__((aligned(1024))) char kb0[L::TILEB];
   __shared__ __attribute__((aligned(1024))) char kb1[L::TILEB];
@@ -516,7 +521,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const TileCoord tc = tile_coord<CAUSAL>(qtiles);
+  const TileCoord tc = tile_coord<CAUSAL, ROWS>(qtiles);
   const int q0 = tc.q0;
   const elt* Qh = q + (int64_t)tc.bh * M * D;
   const elt* Kh = k + (int64_t)tc.bh * N * D;
@@ -527,7 +532,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
   const int qrow = q0 + 32 * w + l32;
   const int wq_first = q0 + 32 * w;
   const int wq_last = min(wq_first + 31, M - 1);
-  const int n_end = CAUSAL ? min(N, q0 + BM + off) : N;
+  const int n_end = CAUSAL ? min(N, q0 + ROWS + off) : N;
   const int ntiles = n_end > 0 ? (n_end + BN - 1) / BN : 0;
   int w_end = CAUSAL ? min(N, wq_last + 1 + off) : N;
   if (wq_first >= M) w_end = 0;
@@ -544,18 +549,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
 
   const int cp_sub = lane / L::SLOTS;
   const int cp_slot = lane % L::SLOTS;
-  // Copy plan: wave w issues the 1 KB copy instructions i = w + 4b (b < BPW).
+  // Copy plan: wave w issues the 1 KB copy instructions i = w + NW*b (b < BPW).
   // Instruction i fills LDS rows i*RPB .. i*RPB+RPB-1; lane l writes slot
-  // l % SLOTS of row i*RPB + l / SLOTS.  Because 4*RPB rows span a whole period
+  // l % SLOTS of row i*RPB + l / SLOTS.  Because NW*RPB rows span whole periods
   // of both swizzles, the logical chunk a lane copies does not depend on b, and
   // one byte offset per matrix serves all of the lane's copies (b only adds
-  // 4*RPB rows).
+  // NW*RPB rows).
   const int cp_row = w * L::RPB + cp_sub;  // row of the lane's first copy (b = 0)
   const int chunk_k = cp_slot ^ L::swz_k(cp_row);
   const int chunk_v = cp_slot ^ L::swz_v(cp_row);
   const unsigned goff_k = (unsigned)((cp_row * D + 8 * chunk_k) * (int)sizeof(elt));
   const unsigned goff_v = (unsigned)((cp_row * D + 8 * chunk_v) * (int)sizeof(elt));
-  constexpr int BSTEP = 4 * L::RPB;  // rows between a lane's consecutive copies
+  constexpr int BSTEP = NW * L::RPB;  // rows between a lane's consecutive copies
+  static_assert(BSTEP % 16 == 0, "swizzle period");
   const int lds_w = __builtin_amdgcn_readfirstlane(w * 1024);  // wave-uniform LDS offset
   auto issue = [&](const elt* src, int n0, char* buf, bool is_v) {
     const int chunk = is_v ? chunk_v : chunk_k;
@@ -566,12 +572,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_pipe_kernel(
 #pragma unroll
       for (int b = 0; b < BPW; ++b)
         copy16_to_lds(base + goff + (unsigned)(b * BSTEP * D * (int)sizeof(elt)),
-                      buf + lds_w + 4096 * b);
+                      buf + lds_w + NW * 1024 * b);
     } else {  // N tail: rows past N copy row N-1 instead (their scores are masked)
 #pragma unroll
       for (int b = 0; b < BPW; ++b) {
         const int key = min(n0 + cp_row + b * BSTEP, N - 1);
-        copy16_to_lds(src + (int64_t)key * D + 8 * chunk, buf + lds_w + 4096 * b);
+        copy16_to_lds(src + (int64_t)key * D + 8 * chunk, buf + lds_w + NW * 1024 * b);
       }
     }
   };
@@ -897,6 +903,7 @@ struct Launch {
   int M, N, D, qtiles;
   float c;
   dim3 grid;
+  int64_t BH;
   hipStream_t stream;
   bool generic;  // force the general kernel (register-staged tiles)
 };
@@ -927,13 +934,23 @@ void launch_f32(const Launch& a) {
                        (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c);
 }
 
+// Waves per workgroup of the fast path (32 query rows each).  At D = 96 and 128
+// a 256-row workgroup halves the K/V copies per FLOP against 128 rows and
+// measured faster; at D = 64 the 128-row workgroup (two per CU) is faster.
+template <int DP>
+constexpr int fast_waves() { return DP == 64 ? 4 : 8; }
+
 template <class T, int DP, bool CAUSAL>
 void launch_lp_fast(const Launch& a) {
   using elt = typename T::elt;
+  constexpr int NW = fast_waves<DP>();
   const int off = CAUSAL ? a.N - a.M : a.N;
-  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP>), a.grid, dim3(NTHREADS), 0, a.stream,
-                     (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N,
-                     off, a.qtiles, a.c);
+  const int rows = 32 * NW;
+  const int qtiles = (a.M + rows - 1) / rows;
+  const dim3 grid((unsigned)(a.BH * qtiles));
+  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW>), grid, dim3(64 * NW), 0, a.stream,
+                     (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M,
+                     a.N, off, qtiles, a.c);
 }
 
 template <class T, bool CAUSAL>
@@ -978,6 +995,7 @@ static int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, flo
   // scale * log2(e) folded once (in double, rounded to fp32) so every exponential is exp2.
   a.c = (float)((double)scale * 1.4426950408889634074);
   a.grid = dim3((unsigned)(B * H * a.qtiles));
+  a.BH = B * H;
   a.stream = (hipStream_t)stream;
   a.generic = generic;
   (void)hipGetLastError();  // clear a stale error so the check below is about this launch
