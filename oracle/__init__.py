@@ -24,6 +24,8 @@ Contents:
 * :mod:`oracle.online` - the streaming (online-softmax) recurrence written out
   step by step, used only to pin the recurrence itself against the definition
   and the pages' printed trace, plus the failure modes the pages name.
+* :mod:`oracle.backward` - gradients of the definition (dQ, dK, dV) and the
+  rebuild of P from the saved LSE, in fp64.
 
 Every function here has at least one pin in ``tests/test_oracle_*.py``; none is
 "parity unpinned".
@@ -31,3 +33,4 @@ Every function here has at least one pin in ``tests/test_oracle_*.py``; none is
 
 from .definition import attention, attention_rows, visible_mask, scale_as_kernel  # noqa: F401
 from .online import online_softmax_trace, tiled_attention  # noqa: F401
+from .backward import attention_bwd, head_bwd, recompute_p  # noqa: F401
