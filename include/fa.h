@@ -1,5 +1,6 @@
 /*
- * fa.h - C ABI of the MI355X (gfx950) FlashAttention forward library (libfa_fwd.so).
+ * fa.h - C ABI of the MI355X (gfx950) FlashAttention library (libfa_fwd.so):
+ * the forward pass and its gradients.
  *
  * The operation is exact scaled dot-product attention with one log-sum-exp per
  * query row, computed tile by tile with the online-softmax recurrence so that no
@@ -96,10 +97,59 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
                   int64_t D, float scale, int causal, int dtype);
 
+/*
+ * fa_bwd - enqueue the gradients of fa_fwd's output o with respect to q, k, v.
+ *
+ * The backward pass by recomputation ("Module 08: FlashAttention and
+ * Memory-Efficient Kernels", section "The backward pass: recompute instead of
+ * store"): only o and lse are kept from the forward pass; every tile of P is
+ * rebuilt on chip as exp(S - LSE) from q and k, and no M x N matrix is stored.
+ * With dO = dout, the chain rule of the definition above (the pages give the
+ * rebuild, not the gradient formulas):
+ *
+ *   dV = P^T dO,  dP = dO V^T,  Delta_i = sum_d dO_id O_id,
+ *   dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Arguments (all DEVICE pointers owned by the caller; the library allocates
+ * nothing and never synchronises):
+ *   q, k, v      as for fa_fwd (read)
+ *   o, lse       fa_fwd's outputs for the same q, k, v, scale, causal (read)
+ *   dout [B, H, M, D]  element type `dtype`: dLoss/dO (read)
+ *   dq   [B, H, M, D], dk [B, H, N, D], dv [B, H, N, D]  element type `dtype` (written)
+ *   delta [B, H, M]    fp32 workspace (written with Delta_i; its contents on
+ *                      return are Delta, usable by the caller)
+ *   scale, causal, stream  as for fa_fwd
+ *   dtype        FA_DTYPE_F16 or FA_DTYPE_BF16 (FA_DTYPE_F32 returns
+ *                FA_ERR_BAD_DTYPE in this version)
+ * P and dS are rounded to `dtype` for their matrix products; accumulation is
+ * fp32; Delta uses the o passed in.  Written buffers must not overlap each
+ * other or any read buffer.
+ *
+ * Returns FA_OK once the work is enqueued.  Argument errors are detected on the
+ * host before any HIP call; then nothing is launched and no output is touched.
+ * B or H zero, or M and N both zero: FA_OK without a launch (pointers may be
+ * NULL).  M == 0 (N > 0): dk and dv are written with zeros (q, o, lse, dout,
+ * dq, delta may be NULL).  N == 0 (M > 0): dq is written with zeros (k, v, dk,
+ * dv may be NULL).  Limits as fa_fwd, plus B*H*ceil(N/128) below 2^31.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta,
+           int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+           float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd_check_args - the host-side validation fa_bwd performs, with the same
+ * arguments (no stream) and return codes, and no HIP call.
+ */
+int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, const void* dq, const void* dk,
+                      const void* dv, const float* delta, int64_t B, int64_t H, int64_t M,
+                      int64_t N, int64_t D, float scale, int causal, int dtype);
+
 /* fa_status_string - a static, human-readable name for a status code. */
 const char* fa_status_string(int status);
 
-/* fa_abi_version - the ABI revision of this header (currently 1). */
+/* fa_abi_version - the ABI revision of this header (currently 2: adds fa_bwd). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

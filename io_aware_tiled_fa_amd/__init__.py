@@ -15,8 +15,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_fwd_general", "fa_check_args", "fa_status_string",
-           "fa_abi_version", "fwd", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "STATUS"]
+__all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_fwd_general", "fa_check_args", "fa_bwd",
+           "fa_bwd_check_args", "fa_status_string", "fa_abi_version", "fwd", "bwd", "DTYPE_F32",
+           "DTYPE_F16", "DTYPE_BF16", "STATUS"]
 
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 STATUS = {
@@ -58,6 +59,11 @@ def load():
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp,
                                   ctypes.c_int, ctypes.c_int]
     lib.fa_check_args.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, i64, fp, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_check_args.argtypes = [vp] * 10 + [i64, i64, i64, i64, i64, fp, ctypes.c_int,
+                                                  ctypes.c_int]
+    lib.fa_bwd_check_args.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -81,6 +87,19 @@ def fa_fwd_general(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream=
 def fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype) -> int:
     return load().fa_check_args(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal),
                                 int(dtype))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D, scale, causal, dtype,
+           stream=None) -> int:
+    """Direct call of the C entry point; pointers are integer device addresses."""
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D, float(scale),
+                         int(causal), int(dtype), stream)
+
+
+def fa_bwd_check_args(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D, scale, causal,
+                      dtype) -> int:
+    return load().fa_bwd_check_args(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D,
+                                    float(scale), int(causal), int(dtype))
 
 
 def fa_status_string(status: int) -> str:
@@ -140,3 +159,52 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     if st != 0:
         raise FaError(st)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None, dq=None,
+        dk=None, dv=None, delta=None, stream=None):
+    """dq, dk, dv = gradients of fwd's o (with its lse) for the incoming gradient dout.
+
+    q [B,H,M,D], k/v [B,H,N,D], o and dout [B,H,M,D] (device tensors of one
+    dtype, float16 or bfloat16), lse [B,H,M] fp32.  Allocates dq, dk, dv and the
+    fp32 workspace ``delta`` [B,H,M] unless given, enqueues fa_bwd on ``stream``
+    (default: torch's current stream) and returns (dq, dk, dv).
+    """
+    import torch
+
+    for t in (q, k, v, o, dout):
+        if t.dim() != 4:
+            raise ValueError("q, k, v, o, dout must be [B, H, seq, D]")
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    if tuple(k.shape) != (B, H, N, D) or tuple(v.shape) != (B, H, N, D):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if tuple(o.shape) != (B, H, M, D) or tuple(dout.shape) != (B, H, M, D):
+        raise ValueError("o and dout must have the shape of q")
+    if tuple(lse.shape) != (B, H, M) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, H, M]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise TypeError("q, k, v, o, dout must share one dtype")
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be device tensors")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                B, H, M, N, D, scale, 1 if causal else 0, code, stream)
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

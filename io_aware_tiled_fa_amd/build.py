@@ -1,4 +1,5 @@
-"""Build libfa_fwd.so in-tree: the gfx950 HIP kernels plus the host-only validation unit.
+"""Build libfa_fwd.so in-tree: the gfx950 HIP kernels (forward and backward) plus the
+host-only validation unit.
 
     python -m io_aware_tiled_fa_amd.build
 
@@ -52,10 +53,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("no host C compiler (gcc) found")
     check_o = os.path.join(BUILD, "fa_check.o")
     fwd_o = os.path.join(BUILD, "fa_fwd.o")
+    bwd_o = os.path.join(BUILD, "fa_bwd.o")
     _run([cc, *C_FLAGS, "-c", os.path.join(CSRC, "fa_check.c"), "-o", check_o], verbose)
     _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_fwd.hip"), "-o", fwd_o], verbose)
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_bwd.hip"), "-o", bwd_o], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, fwd_o, check_o], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, fwd_o, bwd_o, check_o],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -39,6 +39,39 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* o,
   return FA_OK;
 }
 
+int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, const void* dq, const void* dk,
+                      const void* dv, const float* delta, int64_t B, int64_t H, int64_t M,
+                      int64_t N, int64_t D, float scale, int causal, int dtype) {
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return FA_ERR_BAD_DTYPE;
+  if (dtype == FA_DTYPE_F32) return FA_ERR_BAD_DTYPE; /* no fp32 backward in this version */
+  if (B < 0 || H < 0 || M < 0 || N < 0) return FA_ERR_BAD_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_BAD_SHAPE;
+  if (D < 1 || D > 128) return FA_ERR_UNSUPPORTED_D;
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_BAD_SCALE;
+  if (B == 0 || H == 0 || (M == 0 && N == 0)) return FA_OK; /* nothing to compute */
+  if (M > 0 && (q == NULL || o == NULL || lse == NULL || dout == NULL || dq == NULL ||
+                delta == NULL))
+    return FA_ERR_NULL_PTR;
+  if (N > 0 && (k == NULL || v == NULL || dk == NULL || dv == NULL)) return FA_ERR_NULL_PTR;
+  if (M > 0 && (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+                !aligned(lse, 4) || !aligned(delta, 4)))
+    return FA_ERR_MISALIGNED;
+  if (N > 0 && (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16)))
+    return FA_ERR_MISALIGNED;
+  {
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t qt = (M + FA_BLOCK_M - 1) / FA_BLOCK_M;
+    const int64_t kt = (N + FA_BLOCK_M - 1) / FA_BLOCK_M;
+    if (M * D >= lim || N * D >= lim) return FA_ERR_TOO_LARGE;
+    if (B > lim / H) return FA_ERR_TOO_LARGE;
+    if (qt > 0 && B * H >= lim / qt) return FA_ERR_TOO_LARGE;
+    if (kt > 0 && B * H >= lim / kt) return FA_ERR_TOO_LARGE;
+  }
+  return FA_OK;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
@@ -54,4 +87,4 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_abi_version(void) { return 1; }
+int fa_abi_version(void) { return 2; }

@@ -1,0 +1,96 @@
+// fa_device.h - device-side definitions shared by the forward and backward
+// attention kernels for gfx950: element types and their MFMA, the row
+// permutation that lines the 32x32 MFMA accumulator layout up with the next
+// MFMA's operand layout, the XCD-aware workgroup mapping and the lane-pair
+// reductions.  Included by fa_fwd.hip and fa_bwd.hip only.
+#ifndef FA_DEVICE_H
+#define FA_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr float LN2F = 0.693147180559945309417f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct TF16 {
+  using elt = _Float16;
+  using vec8 = f16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+struct TBF16 {
+  using elt = __bf16;
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row of the S^T tile <-> key within a 32-key group: swap bits 2 and 3.
+__device__ __forceinline__ int swap23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Key (relative to the tile's first key, within a 32-key half) held by
+// accumulator register r of a lane in lane-half h.
+__device__ __forceinline__ int key_of_reg(int r, int h) {
+  return 16 * (r >> 3) + 8 * h + (r & 7);
+}
+
+// Which workgroup works on which (batch*head, query tile).
+// Workgroups are handed to the 8 XCDs round-robin (id % 8), and each XCD has
+// its own L2.  The id is remapped so that every XCD walks a contiguous range
+// of (head, query tile) pairs: the query tiles of one head then run on one XCD
+// at about the same time and share that head's K/V in its L2.  Within a head,
+// causal tiles are issued heaviest first (the last query tile sees the most
+// keys), so the light tiles fill the tail.
+struct TileCoord {
+  int bh;
+  int q0;
+};
+constexpr int NXCD = 8;
+template <bool CAUSAL, int ROWS = 128>
+__device__ __forceinline__ TileCoord tile_coord(int qtiles) {
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b % NXCD;
+  const int idx = b / NXCD;
+  const int per = G / NXCD;
+  const int rem = G % NXCD;
+  const int t = xcd * per + min(xcd, rem) + idx;  // contiguous range per XCD
+  TileCoord c;
+  c.bh = t / qtiles;
+  int qt = t - c.bh * qtiles;
+  if (CAUSAL) qt = qtiles - 1 - qt;
+  c.q0 = qt * ROWS;
+  return c;
+}
+
+// Lanes l and l^32 hold the same query row (different keys).  v_permlane32_swap
+// exchanges the two wave halves in one VALU op (no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+}  // namespace
+
+#endif  // FA_DEVICE_H

@@ -26,10 +26,11 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = _declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_check_args", "fa_status_string", "fa_abi_version"}
+    assert set(names) >= {"fa_fwd", "fa_check_args", "fa_bwd", "fa_bwd_check_args",
+                          "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
 
 
 def test_status_strings():
@@ -82,6 +83,54 @@ def test_fa_fwd_rejects_before_any_hip_call(kw, code):
     assert st == code
 
 
+def _bchk(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, delta=P, B=2, H=3, M=100, N=70,
+             D=64, scale=0.125, causal=0, dtype=fa.DTYPE_BF16)
+    a.update(kw)
+    return fa.fa_bwd_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                                a["dk"], a["dv"], a["delta"], a["B"], a["H"], a["M"], a["N"],
+                                a["D"], a["scale"], a["causal"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, OK), ({"dtype": fa.DTYPE_F16}, OK),
+    ({"dtype": fa.DTYPE_F32}, DTYPE),  # no fp32 backward in this version
+    ({"dtype": 3}, DTYPE),
+    ({"B": -1}, SHAPE), ({"N": -1}, SHAPE), ({"causal": 2}, SHAPE),
+    ({"D": 0}, BAD_D), ({"D": 129}, BAD_D), ({"scale": 0.0}, SCALE), ({"scale": math.nan}, SCALE),
+    ({"q": 0}, NULL), ({"o": 0}, NULL), ({"lse": 0}, NULL), ({"dout": 0}, NULL), ({"dq": 0}, NULL),
+    ({"delta": 0}, NULL), ({"k": 0}, NULL), ({"v": 0}, NULL), ({"dk": 0}, NULL), ({"dv": 0}, NULL),
+    ({"dout": P + 8}, ALIGN), ({"dq": P + 2}, ALIGN), ({"dk": P + 4}, ALIGN), ({"dv": P + 8}, ALIGN),
+    ({"delta": P + 2}, ALIGN), ({"delta": P + 4}, OK),
+    ({"B": 0, "q": 0, "k": 0, "v": 0, "o": 0, "lse": 0, "dout": 0, "dq": 0, "dk": 0, "dv": 0,
+      "delta": 0}, OK),
+    ({"M": 0, "N": 0, "q": 0, "k": 0, "v": 0, "o": 0, "lse": 0, "dout": 0, "dq": 0, "dk": 0,
+      "dv": 0, "delta": 0}, OK),
+    # no queries: only dk, dv (zeros) and the K, V they come from are needed
+    ({"M": 0, "q": 0, "o": 0, "lse": 0, "dout": 0, "dq": 0, "delta": 0}, OK),
+    # no keys: only dq (zeros) and the query-side inputs are needed
+    ({"N": 0, "k": 0, "v": 0, "dk": 0, "dv": 0}, OK),
+    ({"M": 1 << 25, "D": 64}, LARGE), ({"N": 1 << 25, "D": 64}, LARGE),
+    ({"B": 1 << 20, "H": 1 << 12, "M": 128, "N": 128}, LARGE),
+])
+def test_bwd_check_args(kw, code):
+    assert _bchk(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": fa.DTYPE_F32}, DTYPE), ({"D": 200}, BAD_D), ({"dq": 0}, NULL),
+    ({"dk": P + 8}, ALIGN), ({"B": 0}, OK), ({"M": 0, "N": 0}, OK),
+])
+def test_fa_bwd_rejects_before_any_hip_call(kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, delta=P, B=2, H=3, M=100, N=70,
+             D=64, scale=0.125, causal=1, dtype=fa.DTYPE_F16)
+    a.update(kw)
+    st = fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                   a["delta"], a["B"], a["H"], a["M"], a["N"], a["D"], a["scale"], a["causal"],
+                   a["dtype"], None)
+    assert st == code
+
+
 def test_python_wrapper_validates_before_the_library(monkeypatch):
     import torch
 
@@ -92,6 +141,11 @@ def test_python_wrapper_validates_before_the_library(monkeypatch):
         fa.fwd(q[0], q[0], q[0])
     with pytest.raises(TypeError):
         fa._dtype_code(torch.zeros(1, dtype=torch.int32))
+    lse = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        fa.bwd(q, q, q, q, lse, q)  # CPU tensors are refused
+    with pytest.raises(ValueError):
+        fa.bwd(q, q, q, q, lse.double(), q)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

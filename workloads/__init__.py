@@ -104,6 +104,18 @@ def make_inputs(w: Workload):
     return q.to(tdt), k.to(tdt), v.to(tdt)
 
 
+def make_dout(w: Workload):
+    """Seeded incoming gradient dL/dO for the backward pass: N(0,1) of the
+    workload's dtype, shape [B,H,M,D], from its own generator (seed + 500000)
+    so that Q, K, V are the same as the forward workload's."""
+    import torch
+
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 500000)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    return torch.randn(w.shape_q(), generator=g, dtype=torch.float32).to(tdt)
+
+
 def sample_rows(M: int, head: int, n: int = 256, seed_base: int = 5000) -> np.ndarray:
     """Seeded sample of query rows for one head (sorted, unique).
 
