@@ -2,6 +2,7 @@
 """Throughput of the attention forward pass (fa_fwd) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--pass fwd|bwd]
 
 A step is one fa_fwd call over the whole batch of the workload: the complete
 hot path (Q tile load, K/V streaming through LDS, both MFMA products, online
@@ -17,6 +18,13 @@ stream the kernel runs on.  Peak: MI355X dense bf16/fp16 MFMA 2516.6 TFLOP/s
 
 The cpu_baseline object times the fp64 CPU oracle (untuned) on a bounded sample
 of the same workload (whole heads, all rows) on this host's cores.
+
+``--pass bwd`` times fa_bwd instead (the forward runs once before the timed
+region and its O and LSE are inputs, as in training).  Its algorithmic work is
+the pages' count for a backward pass with recomputation, five products of
+2*D FLOP per visible (query, key) pair (QK^T again, dP, dV, dQ, dK); the
+kernels execute seven (S and dP are recomputed once more for dQ), which the
+config records.
 """
 
 from __future__ import annotations
@@ -38,6 +46,7 @@ from workloads import (BENCH_WORKLOAD, WORKLOADS, compulsory_bytes, exact_flops,
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 METRIC = "attn fwd TFLOP/s + % of MI355X MFMA peak (N=4096 d=128 causal bf16)"
+METRIC_BWD = "attn bwd TFLOP/s (5 products per pair) + % of MI355X MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -81,6 +90,38 @@ def cpu_baseline(w, qc, kc, vc, budget_s: float = 15.0, max_heads: int = 1 << 30
     }
 
 
+def cpu_baseline_bwd(w, qc, kc, vc, gc, budget_s: float = 15.0):
+    """Time the fp64 oracle's backward on whole heads until ~budget_s."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    qf, kf = qc.reshape(-1, w.M, w.D), kc.reshape(-1, w.N, w.D)
+    vf, gf = vc.reshape(-1, w.N, w.D), gc.reshape(-1, w.M, w.D)
+    t0 = time.perf_counter()
+    done = 0
+    for h in range(qf.shape[0]):
+        oracle.attention_bwd(qf[h], kf[h], vf[h], gf[h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    fl = 2.5 * exact_flops(1, done, w.M, w.N, w.D, w.causal)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} heads, all {w.M} rows, fp64 numpy backward, "
+                  f"{dt:.1f} s wall ({os.cpu_count()} cpus visible)",
+    }
+
+
 def load_traffic(w, kernel_ms):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they match."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -108,6 +149,8 @@ def main():
     ap.add_argument("--workload", default=BENCH_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default, the headline metric) or the backward pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of attention, run a plain device-to-device copy of BYTES "
                          "(3 times); used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -138,6 +181,8 @@ def main():
         return
     fa.load()
     w = WORKLOADS[args.workload]
+    if args.which == "bwd":
+        return bench_bwd(args, w)
     dev = torch.device("cuda:0")
     log(f"workload {w}")
     qc, kc, vc = make_inputs(w)
@@ -223,6 +268,82 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, qc, kc, vc, budget_s=args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def bench_bwd(args, w):
+    import torch
+
+    import io_aware_tiled_fa_amd as fa
+    from workloads import make_dout
+
+    if w.dtype == "f32":
+        print("the backward pass supports fp16 and bf16 workloads", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    log(f"workload {w} (backward)")
+    qc, kc, vc = make_inputs(w)
+    gc = make_dout(w)
+    q, k, v, g = qc.to(dev), kc.to(dev), vc.to(dev), gc.to(dev)
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = {"f16": fa.DTYPE_F16, "bf16": fa.DTYPE_BF16}[w.dtype]
+    ptrs = tuple(t.data_ptr() for t in (q, k, v, o, lse, g, dq, dk, dv, delta))
+
+    def step():
+        st = fa.fa_bwd(*ptrs, w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code,
+                       stream.cuda_stream)
+        if st != 0:
+            raise fa.FaError(st, "fa_bwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / K
+    avg_launch_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    fl_alg = 2.5 * exact_flops(w.B, w.H, w.M, w.N, w.D, w.causal)   # 5 products
+    fl_exec = 3.5 * exact_flops(w.B, w.H, w.M, w.N, w.D, w.causal)  # 7 products
+    peak = PEAK_TFLOPS[w.dtype]
+    tflops = fl_alg / (ms_per_step * 1e-3) / 1e12
+    achieved = fl_alg / (avg_launch_ms * 1e-3) / 1e12
+    log(f"bwd ms/step {ms_per_step:.4f}  avg call {avg_launch_ms:.4f} ms  {tflops:.1f} TFLOP/s "
+        f"algorithmic ({100 * tflops / peak:.1f}% of peak), "
+        f"{fl_exec / (avg_launch_ms * 1e-3) / 1e12:.1f} TFLOP/s executed")
+    out = {
+        "metric": METRIC_BWD, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and incoming gradient, see workloads)",
+        "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
+        "config": {
+            "workload": w.name, "pass": "bwd", "B": w.B, "H": w.H, "M": w.M, "N": w.N, "D": w.D,
+            "causal": w.causal, "flop_algorithmic": fl_alg, "flop_executed": fl_exec,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": "fa_bwd (delta + dkdv + dq kernels, one call)",
+            "avg_launch_ms": round(avg_launch_ms, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle backward on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline_bwd(w, qc, kc, vc, gc, budget_s=args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 
