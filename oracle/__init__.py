@@ -26,6 +26,8 @@ Contents:
   and the pages' printed trace, plus the failure modes the pages name.
 * :mod:`oracle.backward` - gradients of the definition (dQ, dK, dV) and the
   rebuild of P from the saved LSE, in fp64.
+* :mod:`oracle.split` - attention over key chunks and the merge of the partial
+  (O, LSE) pairs by the concatenation algebra.
 
 Every function here has at least one pin in ``tests/test_oracle_*.py``; none is
 "parity unpinned".
@@ -34,3 +36,4 @@ Every function here has at least one pin in ``tests/test_oracle_*.py``; none is
 from .definition import attention, attention_rows, visible_mask, scale_as_kernel  # noqa: F401
 from .online import online_softmax_trace, tiled_attention  # noqa: F401
 from .backward import attention_bwd, head_bwd, recompute_p  # noqa: F401
+from .split import merge_partials, partial_attention, split_attention  # noqa: F401
