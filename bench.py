@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default, the headline metric) or the backward pass")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="forward only: time fa_fwd_splitkv with this many key chunks "
+                         "(0: plain fa_fwd, the headline path)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of attention, run a plain device-to-device copy of BYTES "
                          "(3 times); used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -192,12 +195,21 @@ def main():
     stream = torch.cuda.current_stream(dev)
     code = {"f32": fa.DTYPE_F32, "f16": fa.DTYPE_F16, "bf16": fa.DTYPE_BF16}[w.dtype]
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    if args.splits:
+        wsb = fa.fa_splitkv_workspace_bytes(w.B, w.H, w.M, w.D, args.splits)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
 
-    def step():
-        st = fa.fa_fwd(*ptrs, w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code,
-                       stream.cuda_stream)
-        if st != 0:
-            raise fa.FaError(st)
+        def step():
+            st = fa.fa_fwd_splitkv(*ptrs, w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code,
+                                   args.splits, ws.data_ptr(), wsb, stream.cuda_stream)
+            if st != 0:
+                raise fa.FaError(st, "fa_fwd_splitkv")
+    else:
+        def step():
+            st = fa.fa_fwd(*ptrs, w.B, w.H, w.M, w.N, w.D, w.scale, int(w.causal), code,
+                           stream.cuda_stream)
+            if st != 0:
+                raise fa.FaError(st)
 
     for _ in range(args.warmup):
         step()
@@ -229,7 +241,7 @@ def main():
     tflops = fl_metric / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     achieved = fl_exact / (avg_launch_ms * 1e-3) / 1e12
-    traffic = load_traffic(w, avg_launch_ms)
+    traffic = None if args.splits else load_traffic(w, avg_launch_ms)
     log(f"ms/step {ms_per_step:.4f}  avg launch {avg_launch_ms:.4f} ms  median {med_launch_ms:.4f} ms  "
         f"{tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)  wall {wall:.3f}s")
 
@@ -249,7 +261,7 @@ def main():
         "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "M": w.M, "N": w.N, "D": w.D,
-            "causal": w.causal, "scale": w.scale, "flop_metric": fl_metric,
+            "causal": w.causal, "scale": w.scale, "splits": args.splits, "flop_metric": fl_metric,
             "flop_visible_pairs": fl_exact, "compulsory_bytes": compulsory_bytes(w),
         },
         "roofline": {
@@ -259,7 +271,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": ("fa_fwd_f32_kernel" if w.dtype == "f32" else
+            "kernel": (("fa_fwd_f32_kernel" if w.dtype == "f32" else "fa_fwd_lp_kernel")
+                       + " + fa_merge_kernel (split-KV)" if args.splits else
+                       "fa_fwd_f32_kernel" if w.dtype == "f32" else
                        "fa_fwd_lp_pipe_kernel" if w.D in (64, 96, 128) else "fa_fwd_lp_kernel"),
             "avg_launch_ms": round(avg_launch_ms, 5),
             "hbm_gbs_compulsory": round(compulsory_bytes(w) / (avg_launch_ms * 1e-3) / 1e9, 1),

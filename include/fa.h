@@ -46,8 +46,12 @@ typedef enum {
   FA_ERR_BAD_SCALE = 5,      /* scale not finite or not > 0                               */
   FA_ERR_MISALIGNED = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte       */
   FA_ERR_TOO_LARGE = 7,      /* a per-head extent or the grid exceeds the 32-bit limits   */
-  FA_ERR_HIP = 8             /* the HIP runtime reported an error at launch               */
+  FA_ERR_HIP = 8,            /* the HIP runtime reported an error at launch               */
+  FA_ERR_WORKSPACE = 9       /* fa_fwd_splitkv: workspace NULL, misaligned or too small   */
 } fa_status_t;
+
+/* Largest number of key chunks fa_fwd_splitkv accepts. */
+#define FA_MAX_SPLITS 64
 
 /*
  * fa_fwd - enqueue the attention forward pass on `stream`.
@@ -96,6 +100,56 @@ int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* 
 int fa_check_args(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
                   int64_t D, float scale, int causal, int dtype);
+
+/*
+ * fa_fwd_splitkv - the same operation and results as fa_fwd (O and LSE within
+ * the same accuracy; the summation order differs), computed over key chunks:
+ * the N keys are cut into at most `splits` chunks of whole 64-key tiles, one
+ * launch computes the partial (O_g, LSE_g) of every chunk (normalised over the
+ * chunk's keys, fp32) for every query tile, and a second merges them with the
+ * concatenation algebra ("Module 08: FlashAttention and Memory-Efficient
+ * Kernels", "Tiling and the online softmax": the softmax of a concatenation
+ * follows from the maxima and sums of its pieces):
+ *
+ *   LSE = log sum_g exp(LSE_g),   O = sum_g exp(LSE_g - LSE) O_g.
+ *
+ * It exposes `splits` times more workgroups when B * H * ceil(M/128) alone
+ * cannot fill the GPU (few heads, short query runs, long key runs) -- the
+ * under-filled grid "FlashAttention in Triton" names in "What the H100 run
+ * showed".  The causal mask is the global one (key j visible to row i iff
+ * j <= i + N - M), whichever chunk holds the key.
+ *
+ * Arguments as fa_fwd, plus:
+ *   splits           1 .. FA_MAX_SPLITS
+ *   workspace        device memory owned by the caller, 16-byte aligned, at
+ *                    least fa_splitkv_workspace_bytes(B, H, M, D, splits)
+ *                    bytes (fp32 partials; contents on return unspecified)
+ *   workspace_bytes  its size
+ * Errors as fa_fwd, plus FA_ERR_BAD_SHAPE for `splits` out of range and
+ * FA_ERR_WORKSPACE for a NULL, misaligned or too small workspace (not checked
+ * when nothing is computed: B, H, M or N zero).  Calls that share a workspace
+ * must be ordered (same stream or explicit dependencies).
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                   float scale, int causal, int dtype, int splits, void* workspace,
+                   int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_splitkv_workspace_bytes - bytes of workspace fa_fwd_splitkv needs for
+ * these sizes: splits * B * H * M * (D + 1) * 4.  Returns -1 for negative
+ * sizes, D < 1 or splits < 1.
+ */
+int64_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D, int splits);
+
+/*
+ * fa_splitkv_check_args - the host-side validation fa_fwd_splitkv performs,
+ * with its arguments (no stream) and return codes, and no HIP call.
+ */
+int fa_splitkv_check_args(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                          int64_t D, float scale, int causal, int dtype, int splits,
+                          const void* workspace, int64_t workspace_bytes);
 
 /*
  * fa_bwd - enqueue the gradients of fa_fwd's output o with respect to q, k, v.
@@ -149,7 +203,8 @@ int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o
 /* fa_status_string - a static, human-readable name for a status code. */
 const char* fa_status_string(int status);
 
-/* fa_abi_version - the ABI revision of this header (currently 2: adds fa_bwd). */
+/* fa_abi_version - the ABI revision of this header (currently 3: adds fa_bwd and
+ * fa_fwd_splitkv). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -15,16 +15,18 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_fwd_general", "fa_check_args", "fa_bwd",
+__all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_fwd_general", "fa_check_args",
+           "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_splitkv_check_args", "fa_bwd",
            "fa_bwd_check_args", "fa_status_string", "fa_abi_version", "fwd", "bwd", "DTYPE_F32",
-           "DTYPE_F16", "DTYPE_BF16", "STATUS"]
+           "DTYPE_F16", "DTYPE_BF16", "STATUS", "MAX_SPLITS"]
 
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_BAD_DTYPE",
     4: "FA_ERR_UNSUPPORTED_D", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_MISALIGNED",
-    7: "FA_ERR_TOO_LARGE", 8: "FA_ERR_HIP",
+    7: "FA_ERR_TOO_LARGE", 8: "FA_ERR_HIP", 9: "FA_ERR_WORKSPACE",
 }
+MAX_SPLITS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -59,6 +61,14 @@ def load():
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp,
                                   ctypes.c_int, ctypes.c_int]
     lib.fa_check_args.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.fa_splitkv_workspace_bytes.restype = i64
+    lib.fa_splitkv_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64]
+    lib.fa_splitkv_check_args.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, i64, fp, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd_check_args.argtypes = [vp] * 10 + [i64, i64, i64, i64, i64, fp, ctypes.c_int,
@@ -87,6 +97,23 @@ def fa_fwd_general(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream=
 def fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype) -> int:
     return load().fa_check_args(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal),
                                 int(dtype))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, splits, workspace,
+                   workspace_bytes, stream=None) -> int:
+    """Direct call of the C entry point; pointers are integer device addresses."""
+    return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal),
+                                 int(dtype), int(splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_splitkv_workspace_bytes(B, H, M, D, splits) -> int:
+    return load().fa_splitkv_workspace_bytes(B, H, M, D, int(splits))
+
+
+def fa_splitkv_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, splits, workspace,
+                          workspace_bytes) -> int:
+    return load().fa_splitkv_check_args(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal),
+                                        int(dtype), int(splits), workspace, int(workspace_bytes))
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D, scale, causal, dtype,
@@ -120,12 +147,14 @@ def _dtype_code(t):
 
 
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
-        stream=None, general: bool = False):
+        stream=None, general: bool = False, splits: int | None = None, workspace=None):
     """O, LSE = attention forward of q [B,H,M,D], k/v [B,H,N,D] (device tensors).
 
     Allocates ``o`` (like q) and ``lse`` ([B,H,M] fp32) unless given, enqueues
     fa_fwd on ``stream`` (default: torch's current stream) and returns them.
-    ``general=True`` calls fa_fwd_general instead.
+    ``general=True`` calls fa_fwd_general instead; ``splits=S`` calls
+    fa_fwd_splitkv with S key chunks (allocating the workspace unless a device
+    tensor of enough bytes is given).
     """
     import torch
 
@@ -153,6 +182,17 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    if splits is not None:
+        need = max(fa_splitkv_workspace_bytes(B, H, M, D, splits), 0)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, M, N, D, scale, 1 if causal else 0, code,
+                            splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            stream)
+        if st != 0:
+            raise FaError(st, "fa_fwd_splitkv")
+        return out, lse
     entry = fa_fwd_general if general else fa_fwd
     st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, H, M, N, D, scale, 1 if causal else 0, code, stream)

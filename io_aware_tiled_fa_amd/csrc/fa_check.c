@@ -72,6 +72,24 @@ int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o
   return FA_OK;
 }
 
+int fa_splitkv_check_args(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                          int64_t D, float scale, int causal, int dtype, int splits,
+                          const void* workspace, int64_t workspace_bytes) {
+  const int st = fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (splits < 1 || splits > FA_MAX_SPLITS) return FA_ERR_BAD_SHAPE;
+  if (B == 0 || H == 0 || M == 0 || N == 0) return FA_OK; /* no chunk is computed */
+  if (workspace == NULL || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
+  {
+    const int64_t rows = B * H * M;
+    const int64_t lim = (int64_t)1 << 62;
+    if (rows > lim / ((D + 1) * 4 * (int64_t)splits)) return FA_ERR_TOO_LARGE;
+    if (workspace_bytes < rows * (D + 1) * 4 * (int64_t)splits) return FA_ERR_WORKSPACE;
+  }
+  return FA_OK;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
@@ -83,8 +101,10 @@ const char* fa_status_string(int status) {
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: q/k/v/o need 16-byte, lse 4-byte alignment";
     case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: per-head extent or grid beyond 32-bit limits";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    case FA_ERR_WORKSPACE:
+      return "FA_ERR_WORKSPACE: workspace NULL, not 16-byte aligned, or smaller than required";
     default: return "unknown fa status";
   }
 }
 
-int fa_abi_version(void) { return 2; }
+int fa_abi_version(void) { return 3; }

@@ -151,14 +151,31 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[NT], int n0, int h, int l
     }
 }
 
+// Key chunking of one launch of the general kernels (the split-KV forward):
+// blockIdx.y = g selects keys [g*chunk, min(N, (g+1)*chunk)) of every head, and
+// the outputs of chunk g start g*o_gstride (O) and g*l_gstride (LSE) elements
+// further.  A plain forward launch has one chunk of N keys and zero strides.
+struct KeySplit {
+  int chunk;
+  int64_t o_gstride;
+  int64_t l_gstride;
+};
+
+// Four consecutive output values of a row (16-bit or fp32 outputs).
+template <class OUT>
+__device__ __forceinline__ void store4(OUT* p, const OUT (&y)[4]) {
+  if constexpr (sizeof(OUT) == 4) *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, y);
+  else *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, y);
+}
+
 // ---------------------------------------------------------------------------
 // fp16 / bf16 kernel.  DP: head dim padded to a multiple of 32 (32..128).
 // DFULL: D == DP (rows are whole 16-byte chunks, no column masks).
-template <class T, int DP, bool CAUSAL, bool DFULL>
+template <class T, int DP, bool CAUSAL, bool DFULL, class OUT>
 __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
-    const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
-    float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+    const typename T::elt* __restrict__ v, OUT* __restrict__ o, float* __restrict__ lse, int M,
+    int Ntot, int D, int qtiles, float c, KeySplit ks) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   constexpr int KSTR = DP + 8;          // LDS row stride of K (elements)
@@ -184,13 +201,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
 
   const TileCoord tc = tile_coord<CAUSAL>(qtiles);
   const int q0 = tc.q0;
+  const int nlo = (int)blockIdx.y * ks.chunk;  // first key of this launch's chunk
+  const int N = min(ks.chunk, Ntot - nlo);     // keys in the chunk
   const elt* Qh = q + (int64_t)tc.bh * M * D;
-  const elt* Kh = k + (int64_t)tc.bh * N * D;
-  const elt* Vh = v + (int64_t)tc.bh * N * D;
-  elt* Oh = o + (int64_t)tc.bh * M * D;
-  float* Lh = lse + (int64_t)tc.bh * M;
+  const elt* Kh = k + ((int64_t)tc.bh * Ntot + nlo) * D;
+  const elt* Vh = v + ((int64_t)tc.bh * Ntot + nlo) * D;
+  OUT* Oh = o + (int64_t)blockIdx.y * ks.o_gstride + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)blockIdx.y * ks.l_gstride + (int64_t)tc.bh * M;
 
-  const int off = N - M;  // causal: row i sees keys j <= i + off
+  // causal: row i sees chunk key j (global key nlo + j) iff j <= i + off
+  const int off = Ntot - M - nlo;
   const int qrow = q0 + 32 * w + l32;
   const int wq_first = q0 + 32 * w;
   const int wq_last = min(wq_first + 31, M - 1);
@@ -348,11 +368,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dt + 8 * g + 4 * h;
-        elt y[4];
+        OUT y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (elt)(acc[dt][4 * g + e] * inv);
+        for (int e = 0; e < 4; ++e) y[e] = (OUT)(acc[dt][4 * g + e] * inv);
         if (DFULL) {
-          *reinterpret_cast<u32x2*>(Oh + (int64_t)qrow * D + d0) = __builtin_bit_cast(u32x2, y);
+          store4<OUT>(Oh + (int64_t)qrow * D + d0, y);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -652,7 +672,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
 template <int DP, bool CAUSAL, bool DFULL>
 __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+    float* __restrict__ o, float* __restrict__ lse, int M, int Ntot, int D, int qtiles, float c,
+    KeySplit ks) {
   constexpr int KSTR = DP + 1;
   constexpr int VSTR = DP + 4;
   constexpr int K_ELEMS = BN32 * KSTR;
@@ -673,13 +694,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
 
   const TileCoord tc = tile_coord<CAUSAL>(qtiles);
   const int q0 = tc.q0;
+  const int nlo = (int)blockIdx.y * ks.chunk;  // first key of this launch's chunk
+  const int N = min(ks.chunk, Ntot - nlo);     // keys in the chunk
   const float* Qh = q + (int64_t)tc.bh * M * D;
-  const float* Kh = k + (int64_t)tc.bh * N * D;
-  const float* Vh = v + (int64_t)tc.bh * N * D;
-  float* Oh = o + (int64_t)tc.bh * M * D;
-  float* Lh = lse + (int64_t)tc.bh * M;
+  const float* Kh = k + ((int64_t)tc.bh * Ntot + nlo) * D;
+  const float* Vh = v + ((int64_t)tc.bh * Ntot + nlo) * D;
+  float* Oh = o + (int64_t)blockIdx.y * ks.o_gstride + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)blockIdx.y * ks.l_gstride + (int64_t)tc.bh * M;
 
-  const int off = N - M;
+  const int off = Ntot - M - nlo;
   const int qrow = q0 + 32 * w + l32;
   const int wq_first = q0 + 32 * w;
   const int wq_last = min(wq_first + 31, M - 1);
@@ -814,6 +837,48 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Merge of split-KV partial results: the concatenation algebra of "Module 08:
+// FlashAttention and Memory-Efficient Kernels" ("Tiling and the online
+// softmax": the softmax of a concatenation follows from the maxima and sums of
+// its pieces).  Chunk g left a normalised fp32 O_g and LSE_g per row; then
+//   LSE = m + ln sum_g exp(LSE_g - m)  (m = max_g LSE_g),
+//   O   = sum_g exp(LSE_g - m) O_g / sum_g exp(LSE_g - m).
+// A chunk a row cannot see has LSE_g = -inf and weight 0; a row that sees no
+// key at all keeps O = 0 and LSE = -inf.  One thread per (row, 4 features).
+template <class OUT>
+__global__ __launch_bounds__(NTHREADS) void fa_merge_kernel(
+    const float* __restrict__ opart, const float* __restrict__ lpart, OUT* __restrict__ o,
+    float* __restrict__ lse, int64_t rows, int D, int G, int64_t o_gstride, int64_t l_gstride) {
+  constexpr float LOG2E = 1.44269504088896340736f;
+  const int groups = (D + 3) / 4;
+  const int64_t total = rows * groups;
+  for (int64_t t = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * NTHREADS) {
+    const int64_t row = t / groups;
+    const int d0 = 4 * (int)(t - row * groups);
+    float m = -INFINITY;
+    for (int g = 0; g < G; ++g) m = fmaxf(m, lpart[g * l_gstride + row]);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float tot = 0.0f;
+    if (m != -INFINITY) {
+      for (int g = 0; g < G; ++g) {
+        const float wg = __builtin_amdgcn_exp2f((lpart[g * l_gstride + row] - m) * LOG2E);
+        tot += wg;
+        const float* og = opart + g * o_gstride + row * D + d0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (d0 + e < D) acc[e] = __builtin_fmaf(wg, og[e], acc[e]);
+      }
+    }
+    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (d0 + e < D) o[row * D + d0 + e] = (OUT)(acc[e] * inv);
+    if (d0 == 0) lse[row] = tot > 0.0f ? m + LN2F * __builtin_amdgcn_logf(tot) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host dispatch.
 
 struct Launch {
@@ -833,27 +898,28 @@ struct Launch {
 template <class T, int DP, bool CAUSAL>
 void launch_lp(const Launch& a) {
   using elt = typename T::elt;
-  const bool full = a.D == DP;
-  if (full)
-    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, true>), a.grid, dim3(NTHREADS), 0,
+  const KeySplit ks{a.N, 0, 0};
+  if (a.D == DP)
+    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, true, elt>), a.grid, dim3(NTHREADS), 0,
                        a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
-                       a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+                       a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
   else
-    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, false>), a.grid, dim3(NTHREADS), 0,
+    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, false, elt>), a.grid, dim3(NTHREADS), 0,
                        a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
-                       a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+                       a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
 }
 
 template <int DP, bool CAUSAL>
 void launch_f32(const Launch& a) {
+  const KeySplit ks{a.N, 0, 0};
   if (a.D == DP)
     hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, true>), a.grid, dim3(NTHREADS), 0,
                        a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
   else
     hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, false>), a.grid, dim3(NTHREADS), 0,
                        a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c);
+                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
 }
 
 // Waves per workgroup of the fast path (32 query rows each).  At D = 96 and 128
@@ -894,6 +960,47 @@ void dispatch_f32(const Launch& a) {
   else if (a.D <= 64) launch_f32<64, CAUSAL>(a);
   else if (a.D <= 96) launch_f32<96, CAUSAL>(a);
   else launch_f32<128, CAUSAL>(a);
+}
+
+// Split-KV partials: chunk g of every head's keys into the fp32 workspace.
+template <class T, int DP, bool CAUSAL>
+void launch_lp_split(const Launch& a, const KeySplit& ks, int G, float* opart, float* lpart) {
+  using elt = typename T::elt;
+  const dim3 grid(a.grid.x, (unsigned)G);
+  if (a.D == DP)
+    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, true, float>), grid, dim3(NTHREADS), 0,
+                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart,
+                       a.M, a.N, a.D, a.qtiles, a.c, ks);
+  else
+    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, false, float>), grid, dim3(NTHREADS), 0,
+                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart,
+                       a.M, a.N, a.D, a.qtiles, a.c, ks);
+}
+template <int DP, bool CAUSAL>
+void launch_f32_split(const Launch& a, const KeySplit& ks, int G, float* opart, float* lpart) {
+  const dim3 grid(a.grid.x, (unsigned)G);
+  if (a.D == DP)
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, true>), grid, dim3(NTHREADS), 0, a.stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, opart, lpart, a.M,
+                       a.N, a.D, a.qtiles, a.c, ks);
+  else
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, false>), grid, dim3(NTHREADS), 0, a.stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, opart, lpart, a.M,
+                       a.N, a.D, a.qtiles, a.c, ks);
+}
+template <class T, bool CAUSAL>
+void dispatch_lp_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
+  if (a.D <= 32) launch_lp_split<T, 32, CAUSAL>(a, ks, G, op, lp);
+  else if (a.D <= 64) launch_lp_split<T, 64, CAUSAL>(a, ks, G, op, lp);
+  else if (a.D <= 96) launch_lp_split<T, 96, CAUSAL>(a, ks, G, op, lp);
+  else launch_lp_split<T, 128, CAUSAL>(a, ks, G, op, lp);
+}
+template <bool CAUSAL>
+void dispatch_f32_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
+  if (a.D <= 32) launch_f32_split<32, CAUSAL>(a, ks, G, op, lp);
+  else if (a.D <= 64) launch_f32_split<64, CAUSAL>(a, ks, G, op, lp);
+  else if (a.D <= 96) launch_f32_split<96, CAUSAL>(a, ks, G, op, lp);
+  else launch_f32_split<128, CAUSAL>(a, ks, G, op, lp);
 }
 
 }  // namespace
@@ -945,4 +1052,78 @@ extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void*
                               int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
                               int causal, int dtype, void* stream) {
   return fa_fwd_impl(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream, true);
+}
+
+extern "C" int64_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D,
+                                              int splits) {
+  if (B < 0 || H < 0 || M < 0 || D < 1 || splits < 1) return -1;
+  return (int64_t)splits * B * H * M * (D + 1) * (int64_t)sizeof(float);
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                              int causal, int dtype, int splits, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+  const int st = fa_splitkv_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype,
+                                       splits, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  if (B == 0 || H == 0 || M == 0) return FA_OK;
+  if (N == 0) return fa_fwd_impl(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream,
+                                 true);  // every row is empty: no chunk to merge
+  // Chunks of ceil(N / splits) keys, rounded up to whole 64-key tiles.
+  int64_t chunk = (N + splits - 1) / splits;
+  chunk = (chunk + 63) / 64 * 64;
+  const int G = (int)((N + chunk - 1) / chunk);
+  const int64_t rows = B * H * M;
+  float* opart = (float*)workspace;
+  float* lpart = opart + (int64_t)G * rows * D;
+  Launch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.D = (int)D;
+  a.qtiles = (int)((M + BM - 1) / BM);
+  a.c = (float)((double)scale * 1.4426950408889634074);
+  a.grid = dim3((unsigned)(B * H * a.qtiles));
+  a.BH = B * H;
+  a.stream = (hipStream_t)stream;
+  a.generic = true;
+  const KeySplit ks{(int)chunk, rows * D, rows};
+  (void)hipGetLastError();
+  switch (dtype) {
+    case FA_DTYPE_F16:
+      causal ? dispatch_lp_split<TF16, true>(a, ks, G, opart, lpart)
+             : dispatch_lp_split<TF16, false>(a, ks, G, opart, lpart);
+      break;
+    case FA_DTYPE_BF16:
+      causal ? dispatch_lp_split<TBF16, true>(a, ks, G, opart, lpart)
+             : dispatch_lp_split<TBF16, false>(a, ks, G, opart, lpart);
+      break;
+    default:
+      causal ? dispatch_f32_split<true>(a, ks, G, opart, lpart)
+             : dispatch_f32_split<false>(a, ks, G, opart, lpart);
+      break;
+  }
+  const int64_t work = rows * ((D + 3) / 4);
+  const int64_t blocks = (work + NTHREADS - 1) / NTHREADS;
+  const dim3 mgrid((unsigned)(blocks < 65536 ? blocks : 65536));
+  switch (dtype) {
+    case FA_DTYPE_F16:
+      hipLaunchKernelGGL((fa_merge_kernel<_Float16>), mgrid, dim3(NTHREADS), 0, a.stream, opart,
+                         lpart, (_Float16*)o, lse, rows, (int)D, G, rows * D, rows);
+      break;
+    case FA_DTYPE_BF16:
+      hipLaunchKernelGGL((fa_merge_kernel<__bf16>), mgrid, dim3(NTHREADS), 0, a.stream, opart,
+                         lpart, (__bf16*)o, lse, rows, (int)D, G, rows * D, rows);
+      break;
+    default:
+      hipLaunchKernelGGL((fa_merge_kernel<float>), mgrid, dim3(NTHREADS), 0, a.stream, opart,
+                         lpart, (float*)o, lse, rows, (int)D, G, rows * D, rows);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

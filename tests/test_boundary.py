@@ -27,10 +27,11 @@ def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = _declared_functions()
     assert set(names) >= {"fa_fwd", "fa_check_args", "fa_bwd", "fa_bwd_check_args",
+                          "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_splitkv_check_args",
                           "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
 
 
 def test_status_strings():
@@ -129,6 +130,52 @@ def test_fa_bwd_rejects_before_any_hip_call(kw, code):
                    a["delta"], a["B"], a["H"], a["M"], a["N"], a["D"], a["scale"], a["causal"],
                    a["dtype"], None)
     assert st == code
+
+
+WS = 1 << 20  # a fake 16-byte aligned workspace address
+
+
+def _schk(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, M=100, N=70, D=64, scale=0.125, causal=0,
+             dtype=fa.DTYPE_BF16, splits=4, ws=WS, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = fa.fa_splitkv_workspace_bytes(a["B"], a["H"], a["M"], a["D"], a["splits"])
+    return fa.fa_splitkv_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                    a["M"], a["N"], a["D"], a["scale"], a["causal"], a["dtype"],
+                                    a["splits"], a["ws"], a["wsb"])
+
+
+WORKSPACE = 9
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, OK), ({"dtype": fa.DTYPE_F32}, OK), ({"splits": 1}, OK), ({"splits": 64}, OK),
+    ({"splits": 0}, SHAPE), ({"splits": 65}, SHAPE), ({"splits": -3}, SHAPE),
+    ({"ws": 0}, WORKSPACE), ({"ws": WS + 8}, WORKSPACE), ({"wsb": 1000}, WORKSPACE),
+    ({"D": 0}, BAD_D), ({"q": 0}, NULL), ({"scale": -1.0}, SCALE),  # fa_fwd's checks come first
+    ({"N": 0, "k": 0, "v": 0, "ws": 0, "wsb": 0}, OK),  # no keys: no chunk, no workspace needed
+    ({"M": 0, "q": 0, "o": 0, "lse": 0, "ws": 0, "wsb": 0}, OK),
+])
+def test_splitkv_check_args(kw, code):
+    assert _schk(**kw) == code
+
+
+def test_splitkv_workspace_bytes():
+    assert fa.fa_splitkv_workspace_bytes(2, 3, 100, 64, 4) == 4 * 2 * 3 * 100 * 65 * 4
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 1, 1) == 8
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 0, 1) == -1
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 8, 0) == -1
+
+
+def test_fa_fwd_splitkv_rejects_before_any_hip_call():
+    wsb = fa.fa_splitkv_workspace_bytes(2, 3, 100, 64, 4)
+    assert fa.fa_fwd_splitkv(P, P, P, P, P, 2, 3, 100, 70, 64, 0.125, 1, fa.DTYPE_F16, 4, 0, wsb,
+                             None) == WORKSPACE
+    assert fa.fa_fwd_splitkv(P, P, P, P, P, 2, 3, 100, 70, 64, 0.125, 1, fa.DTYPE_F16, 99, WS, wsb,
+                             None) == SHAPE
+    assert fa.fa_fwd_splitkv(P, P, P, P, P, 0, 3, 100, 70, 64, 0.125, 1, fa.DTYPE_F16, 4, 0, 0,
+                             None) == OK
 
 
 def test_python_wrapper_validates_before_the_library(monkeypatch):
