@@ -432,15 +432,16 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, char* lds_block) {
 // its own pair of LDS buffers (same 64 KB as two K+V stages), and the copy
 // of K(j+2) and V(j+1) is in flight during step j.
 //
-// One instantiation serves causal and non-causal calls: `off` is the causal
-// diagonal offset (key j visible to row i iff j <= i + off), N - M for a
-// bottom-right causal mask and N for no mask (no row can reach it, so only the
-// N tail is ever masked).
-template <class T, int DP, int NW>
+// One instantiation serves causal and non-causal calls: `off_all` is the
+// causal diagonal offset (key j visible to row i iff j <= i + off_all), N - M
+// for a bottom-right causal mask and N for no mask (no row can reach it, so
+// only the N tail is ever masked).  With a key split (blockIdx.y = chunk) the
+// same offset, less the chunk's first key, applies to the chunk's keys.
+template <class T, int DP, int NW, class OUT>
 __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
-    const typename T::elt* __restrict__ v, typename T::elt* __restrict__ o,
-    float* __restrict__ lse, int M, int N, int off, int qtiles, float c) {
+    const typename T::elt* __restrict__ v, OUT* __restrict__ o, float* __restrict__ lse, int M,
+    int Ntot, int off_all, int qtiles, float c, KeySplit ks) {
   constexpr bool CAUSAL = true;  // masking logic always on; `off` decides what it masks
   constexpr int D = DP;          // the dispatcher routes only D == DP here
   using elt = typename T::elt;
@@ -465,11 +466,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
 
   const TileCoord tc = tile_coord<CAUSAL, ROWS>(qtiles);
   const int q0 = tc.q0;
+  const int nlo = (int)blockIdx.y * ks.chunk;  // first key of this launch's chunk
+  const int N = min(ks.chunk, Ntot - nlo);     // keys in the chunk
+  const int off = off_all - nlo;               // chunk key j visible to row i iff j <= i + off
   const elt* Qh = q + (int64_t)tc.bh * M * D;
-  const elt* Kh = k + (int64_t)tc.bh * N * D;
-  const elt* Vh = v + (int64_t)tc.bh * N * D;
-  elt* Oh = o + (int64_t)tc.bh * M * D;
-  float* Lh = lse + (int64_t)tc.bh * M;
+  const elt* Kh = k + ((int64_t)tc.bh * Ntot + nlo) * D;
+  const elt* Vh = v + ((int64_t)tc.bh * Ntot + nlo) * D;
+  OUT* Oh = o + (int64_t)blockIdx.y * ks.o_gstride + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)blockIdx.y * ks.l_gstride + (int64_t)tc.bh * M;
 
   const int qrow = q0 + 32 * w + l32;
   const int wq_first = q0 + 32 * w;
@@ -655,10 +659,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dt + 8 * g + 4 * h;
-        elt y[4];
+        OUT y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (elt)(acc[dt][4 * g + e] * inv);
-        *reinterpret_cast<u32x2*>(Oh + (int64_t)qrow * D + d0) = __builtin_bit_cast(u32x2, y);
+        for (int e = 0; e < 4; ++e) y[e] = (OUT)(acc[dt][4 * g + e] * inv);
+        store4<OUT>(Oh + (int64_t)qrow * D + d0, y);
       }
     if (h == 0)
       Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
@@ -936,9 +940,25 @@ void launch_lp_fast(const Launch& a) {
   const int rows = 32 * NW;
   const int qtiles = (a.M + rows - 1) / rows;
   const dim3 grid((unsigned)(a.BH * qtiles));
-  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW>), grid, dim3(64 * NW), 0, a.stream,
+  const KeySplit ks{a.N, 0, 0};
+  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, elt>), grid, dim3(64 * NW), 0, a.stream,
                      (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M,
-                     a.N, off, qtiles, a.c);
+                     a.N, off, qtiles, a.c, ks);
+}
+
+// Split-KV partials on the fast path (fp32 outputs into the workspace).
+template <class T, int DP, bool CAUSAL>
+void launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, float* opart,
+                          float* lpart) {
+  using elt = typename T::elt;
+  constexpr int NW = fast_waves<DP>();
+  const int off = CAUSAL ? a.N - a.M : a.N;
+  const int rows = 32 * NW;
+  const int qtiles = (a.M + rows - 1) / rows;
+  const dim3 grid((unsigned)(a.BH * qtiles), (unsigned)G);
+  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, float>), grid, dim3(64 * NW), 0,
+                     a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart,
+                     a.M, a.N, off, qtiles, a.c, ks);
 }
 
 template <class T, bool CAUSAL>
@@ -990,6 +1010,9 @@ void launch_f32_split(const Launch& a, const KeySplit& ks, int G, float* opart, 
 }
 template <class T, bool CAUSAL>
 void dispatch_lp_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
+  if (a.D == 128) return launch_lp_fast_split<T, 128, CAUSAL>(a, ks, G, op, lp);
+  if (a.D == 96) return launch_lp_fast_split<T, 96, CAUSAL>(a, ks, G, op, lp);
+  if (a.D == 64) return launch_lp_fast_split<T, 64, CAUSAL>(a, ks, G, op, lp);
   if (a.D <= 32) launch_lp_split<T, 32, CAUSAL>(a, ks, G, op, lp);
   else if (a.D <= 64) launch_lp_split<T, 64, CAUSAL>(a, ks, G, op, lp);
   else if (a.D <= 96) launch_lp_split<T, 96, CAUSAL>(a, ks, G, op, lp);
