@@ -495,6 +495,204 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dQ on the fast path (fp16/bf16, D in {64, 96, 128}): the forward's
+// pipelined layout.  NW waves x 32 query rows per workgroup (NW = 8 at D = 96
+// and 128, 4 at D = 64); 64-key K and V tiles go HBM -> LDS by global_load_lds
+// (no VGPR staging), double-buffered, one barrier per tile.  Both tiles use the
+// K-operand swizzle of FastLayout, which keeps the row reads of S^T = K Q^T and
+// dP^T = V dO^T and the transposing reads of K^T (for dQ^T += K^T dS^T)
+// bank-conflict free.
+template <class T, int DP, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
+    const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
+    const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dq,
+    int M, int N, int qtiles, float c, float scale, int causal) {
+  using elt = typename T::elt;
+  using vec8 = typename T::vec8;
+  using L = FastLayout<DP>;
+  constexpr int D = DP;
+  constexpr int KK = DP / 16;
+  constexpr int DT = DP / 32;
+  constexpr int BPW = L::NBLK / NW;
+  constexpr int ROWS = 32 * NW;
+  static_assert(L::NBLK % NW == 0, "copy plan");
+
+  __shared__ __attribute__((aligned(1024))) char kb0[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb1[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb0[L::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb1[L::TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<true, ROWS>(qtiles);  // heaviest causal tiles first
+  const int q0 = tc.q0;
+  const elt* Qh = q + (int64_t)tc.bh * M * D;
+  const elt* Kh = k + (int64_t)tc.bh * N * D;
+  const elt* Vh = v + (int64_t)tc.bh * N * D;
+  const elt* Gh = dout + (int64_t)tc.bh * M * D;
+  const float* Lh = lse + (int64_t)tc.bh * M;
+  const float* Dh = delta + (int64_t)tc.bh * M;
+  elt* dQh = dq + (int64_t)tc.bh * M * D;
+
+  // Causal: key j visible to row i iff j <= i + off; without the mask `off` = N
+  // (no row reaches it, so only the N tail is masked).
+  const int off = causal ? N - M : N;
+  const int qrow = q0 + 32 * w + l32;
+  const int wq_first = q0 + 32 * w;
+  const int wq_last = min(wq_first + 31, M - 1);
+  const int n_end = min(N, q0 + ROWS + off);
+  const int ntiles = n_end > 0 ? (n_end + 63) / 64 : 0;
+  int w_end = min(N, wq_last + 1 + off);
+  if (wq_first >= M) w_end = 0;
+  const int w_tiles = w_end > 0 ? (w_end + 63) / 64 : 0;
+  const int lim = min(N, qrow + off + 1);
+
+  vec8 qb[KK], gb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qb[kk] = load_row8<T, true>(Qh, qrow, M, D, 16 * kk + 8 * h);
+    gb[kk] = load_row8<T, true>(Gh, qrow, M, D, 16 * kk + 8 * h);
+  }
+  float l2 = 0.0f, dl = 0.0f;
+  if (qrow < M) {
+    l2 = Lh[qrow] * LOG2E;
+    dl = Dh[qrow];
+  }
+  if (l2 == -INFINITY) l2 = 0.0f;  // no visible key: every score of the row is masked
+  f32x16 dqa[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqa[dt] = f32x16{};
+
+  // Copy plan as in the forward's pipelined kernel, one swizzle for K and V.
+  const int cp_sub = lane / L::SLOTS;
+  const int cp_slot = lane % L::SLOTS;
+  const int cp_row = w * L::RPB + cp_sub;
+  const int chunk = cp_slot ^ L::swz_k(cp_row);
+  const unsigned goff = (unsigned)((cp_row * D + 8 * chunk) * (int)sizeof(elt));
+  constexpr int BSTEP = NW * L::RPB;
+  static_assert(BSTEP % 16 == 0, "swizzle period");
+  const int lds_w = __builtin_amdgcn_readfirstlane(w * 1024);
+  auto issue = [&](const elt* src, int n0, char* buf) {
+    if (chunk >= L::CPR) return;  // D = 96: slots 12..15 of a row hold no data
+    if (n0 + 64 <= N) {
+      const char* base = reinterpret_cast<const char*>(src + (int64_t)n0 * D);
+#pragma unroll
+      for (int b = 0; b < BPW; ++b)
+        copy16_to_lds(base + goff + (unsigned)(b * BSTEP * D * (int)sizeof(elt)),
+                      buf + lds_w + NW * 1024 * b);
+    } else {  // N tail: rows past N copy row N-1 instead (their scores are masked)
+#pragma unroll
+      for (int b = 0; b < BPW; ++b) {
+        const int key = min(n0 + cp_row + b * BSTEP, N - 1);
+        copy16_to_lds(src + (int64_t)key * D + 8 * chunk, buf + lds_w + NW * 1024 * b);
+      }
+    }
+  };
+
+  // Row reads (A operands of S^T and dP^T, rows in swap-2-3 order).
+  const int krow = swap23(l32);
+  int koff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * L::ROWB + 16 * ((2 * kk + h) ^ L::swz_k(krow));
+  // Transposing reads of K (A operand of dQ^T): lane j of a 16-lane group
+  // addresses row 8h + j/4 (+4 for the second read) of a 16-key chunk and 4
+  // features at 32dt + 16*dhalf + 4*(j%4).  The swizzle does not depend on the
+  // 16-key chunk, so that offset is an immediate.
+  const int dhalf = (lane >> 4) & 1;
+  const int j16 = lane & 15;
+  int toff[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 8 * h + (j16 >> 2) + 4 * hi;
+      const int ch = 4 * dt + 2 * dhalf + ((j16 & 3) >> 1);
+      toff[dt][hi] = row * L::ROWB + 16 * (ch ^ L::swz_k(row)) + 8 * (j16 & 1);
+    }
+
+  auto step = [&](int j, const char* kbuf, const char* vbuf) {
+    const int n0 = j * 64;
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const vec8 ak = *reinterpret_cast<const vec8*>(kbuf + koff[kk] + 32 * t * L::ROWB);
+        const vec8 av = *reinterpret_cast<const vec8*>(vbuf + koff[kk] + 32 * t * L::ROWB);
+        s[t] = T::mfma(ak, qb[kk], s[t]);
+        dp[t] = T::mfma(av, gb[kk], dp[t]);
+      }
+    }
+    const bool need_mask = (n0 + 64 > N) || (n0 + 63 > wq_first + off);
+    f32x16 ds[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -l2));
+        if (need_mask) pr = (n0 + 32 * t + key_of_reg(r, h) < lim) ? pr : 0.0f;
+        ds[t][r] = pr * (dp[t][r] - dl);
+      }
+    vec8 dsb[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      f32x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = ds[cc >> 1][8 * (cc & 1) + e];
+      dsb[cc] = __builtin_convertvector(f, vec8);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(kbuf + toff[dt][0] + 16 * cc * L::ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(kbuf + toff[dt][1] + 16 * cc * L::ROWB));
+        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dqa[dt] = T::mfma(a, dsb[cc], dqa[dt]);
+      }
+  };
+
+  if (ntiles > 0) {
+    issue(Kh, 0, kb0);
+    issue(Vh, 0, vb0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) {
+      issue(Kh, (j + 1) * 64, kb1);
+      issue(Vh, (j + 1) * 64, vb1);
+    }
+    if (j < w_tiles) step(j, kb0, vb0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) {
+      issue(Kh, (j + 2) * 64, kb0);
+      issue(Vh, (j + 2) * 64, vb0);
+    }
+    if (j + 1 < w_tiles) step(j + 1, kb1, vb1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (qrow < M) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store_row4<T, true>(dQh, qrow, D, 32 * dt + 8 * g + 4 * h, dqa[dt], g, scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host dispatch.
 
 struct BwdArgs {
@@ -519,6 +717,17 @@ void launch_bwd_tiles(const BwdArgs& a) {
                        ktiles, a.c, a.scale);
   }
   if (a.M > 0) {
+    if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
+      if (a.N > 0) {
+        constexpr int NW = DP == 64 ? 4 : 8;
+        const int qtiles = (a.M + 32 * NW - 1) / (32 * NW);
+        hipLaunchKernelGGL((fa_bwd_dq_fast_kernel<T, DP, NW>), dim3((unsigned)(a.BH * qtiles)),
+                           dim3(64 * NW), 0, a.stream, (const elt*)a.q, (const elt*)a.k,
+                           (const elt*)a.v, (const elt*)a.dout, a.lse, a.delta, (elt*)a.dq, a.M,
+                           a.N, qtiles, a.c, a.scale, CAUSAL ? 1 : 0);
+        return;
+      }
+    }
     const int qtiles = (a.M + BMQ - 1) / BMQ;
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, DP, CAUSAL, DFULL>), dim3((unsigned)(a.BH * qtiles)),
                        dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,

@@ -91,6 +91,42 @@ __device__ __forceinline__ float pair_sum(float x) {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// Direct-to-LDS tile layout for fp16/bf16 with D in {64, 96, 128}: K and V tiles are copied from
+// HBM straight into LDS (global_load_lds, 16 B per lane, no VGPR staging), in
+// their natural row-major layout with a per-row XOR swizzle of the 16-byte
+// chunks.  The K operand of S^T is one ds_read_b128 per lane and k-step; the
+// V^T operand of O^T is read transposed out of row-major V with two
+// ds_read_b64_tr_b16 per MFMA (each lane of a 16-lane group receives one
+// column of a 4-row x 4-column block).  The swizzle makes both read patterns
+// bank-conflict free: 16 consecutive rows hit 16 distinct chunk positions for
+// the K reads, and the 4 rows of a transpose read land in 4 distinct 64-byte
+// groups of banks.
+template <int DP>
+struct FastLayout {
+  static constexpr int ROWB = DP == 64 ? 128 : 256;  // LDS bytes per K/V row
+  static constexpr int CPR = DP / 8;                  // 16-byte chunks holding data
+  static constexpr int SLOTS = ROWB / 16;             // 16-byte slots per row
+  static constexpr int TILEB = 64 * ROWB;             // one 64-row K (or V) tile
+  static constexpr int RPB = 1024 / ROWB;             // rows per 1 KB copy instruction
+  static constexpr int NBLK = TILEB / 1024;           // copy instructions per tile matrix
+  // Physical slot of logical chunk c in row r is c ^ swz(r).
+  // K: the 16 rows of a score-MFMA read land on 16 distinct slots.
+  static __device__ __forceinline__ int swz_k(int r) {
+    return DP == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+  }
+  // V: the 4 rows of a transpose read land in 4 distinct 64-byte bank groups;
+  // depends only on r mod 4 so that rows 4 apart share the pattern.
+  static __device__ __forceinline__ int swz_v(int r) {
+    return DP == 64 ? (((r >> 1) & 1) << 2) : ((r & 3) << 2);
+  }
+};
+
+
+__device__ __forceinline__ void copy16_to_lds(const void* g, char* lds_block) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds_block, 16, 0, 0);
+}
+
 }  // namespace
 
 #endif  // FA_DEVICE_H
