@@ -301,7 +301,7 @@ def bench_bwd(args, w):
     q, k, v, g = qc.to(dev), kc.to(dev), vc.to(dev), gc.to(dev)
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
+    delta = torch.empty((2, w.B, w.H, w.M), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     code = {"f16": fa.DTYPE_F16, "bf16": fa.DTYPE_BF16}[w.dtype]
     ptrs = tuple(t.data_ptr() for t in (q, k, v, o, lse, g, dq, dk, dv, delta))

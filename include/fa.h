@@ -170,8 +170,10 @@ int fa_splitkv_check_args(const void* q, const void* k, const void* v, const voi
  *   o, lse       fa_fwd's outputs for the same q, k, v, scale, causal (read)
  *   dout [B, H, M, D]  element type `dtype`: dLoss/dO (read)
  *   dq   [B, H, M, D], dk [B, H, N, D], dv [B, H, N, D]  element type `dtype` (written)
- *   delta [B, H, M]    fp32 workspace (written with Delta_i; its contents on
- *                      return are Delta, usable by the caller)
+ *   delta [2, B, H, M] fp32 workspace (written; on return delta[0] holds
+ *                      -Delta_i and delta[1] holds -LSE_i / scale, 0 where
+ *                      LSE_i = -inf: per-row terms the kernels fold into
+ *                      their accumulators)
  *   scale, causal, stream  as for fa_fwd
  *   dtype        FA_DTYPE_F16 or FA_DTYPE_BF16 (FA_DTYPE_F32 returns
  *                FA_ERR_BAD_DTYPE in this version)
@@ -203,8 +205,8 @@ int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o
 /* fa_status_string - a static, human-readable name for a status code. */
 const char* fa_status_string(int status);
 
-/* fa_abi_version - the ABI revision of this header (currently 3: adds fa_bwd and
- * fa_fwd_splitkv). */
+/* fa_abi_version - the ABI revision of this header (currently 4: 3 added fa_bwd
+ * and fa_fwd_splitkv; 4 doubled fa_bwd's workspace to [2, B, H, M]). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

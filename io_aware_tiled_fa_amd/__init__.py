@@ -207,8 +207,8 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
 
     q [B,H,M,D], k/v [B,H,N,D], o and dout [B,H,M,D] (device tensors of one
     dtype, float16 or bfloat16), lse [B,H,M] fp32.  Allocates dq, dk, dv and the
-    fp32 workspace ``delta`` [B,H,M] unless given, enqueues fa_bwd on ``stream``
-    (default: torch's current stream) and returns (dq, dk, dv).
+    fp32 workspace ``delta`` [2,B,H,M] unless given, enqueues fa_bwd on
+    ``stream`` (default: torch's current stream) and returns (dq, dk, dv).
     """
     import torch
 
@@ -237,7 +237,9 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if delta is None:
-        delta = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+        delta = torch.empty((2, B, H, M), dtype=torch.float32, device=q.device)
+    elif delta.dtype != torch.float32 or delta.numel() < 2 * B * H * M or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous fp32 workspace of at least 2*B*H*M elements")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):

@@ -45,15 +45,30 @@ constexpr int BQ = 64;           // queries per dkdv step
 constexpr int BMQ = 128;         // queries per dq workgroup
 constexpr int BNK = 64;          // keys per dq step
 constexpr float LOG2E = 1.44269504088896340736f;
+#ifndef DKDV_NBUF
+#define DKDV_NBUF 3  // query-tile buffers of the fast dK/dV kernel (copies run NBUF - 2 tiles ahead)
+#endif
+#ifndef DKDV_LA1
+#define DKDV_LA1 4   // fast dK/dV: MFMAs whose row reads are issued ahead (stage 1)
+#endif
+#ifndef DKDV_LA2
+#define DKDV_LA2 4   // fast dK/dV: MFMAs whose transposing reads are issued ahead (stage 2)
+#endif
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Delta_i = sum_d dO[i, d] * O[i, d] in fp32; 16 lanes per row.
+// Per query row, into the two halves of the workspace:
+//   ws[row]        = -Delta_i, Delta_i = sum_d dO[i, d] * O[i, d] in fp32;
+//   ws[rows + row] = -L_i / scale (0 where L_i = -inf: the row sees no key).
+// The fast dK/dV kernel loads them as the initial values of the dP and S
+// accumulators, so that the MFMAs leave dP - Delta and S - L / scale, and
+// P = exp2(c * acc) with c = scale * log2(e).  16 lanes per row.
 template <class T>
 __global__ __launch_bounds__(BT) void fa_bwd_delta_kernel(const typename T::elt* __restrict__ o,
                                                           const typename T::elt* __restrict__ dout,
-                                                          float* __restrict__ delta, int64_t rows,
-                                                          int D) {
+                                                          const float* __restrict__ lse,
+                                                          float* __restrict__ ws, int64_t rows,
+                                                          int D, float scale) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   const int sub = threadIdx.x >> 4;
@@ -77,7 +92,11 @@ __global__ __launch_bounds__(BT) void fa_bwd_delta_kernel(const typename T::elt*
     }
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-    if (row < rows && l16 == 0) delta[row] = acc;
+    if (row < rows && l16 == 0) {
+      ws[row] = -acc;
+      const float x = lse[row];
+      ws[rows + row] = x == -INFINITY ? 0.0f : -(x / scale);
+    }
   }
 }
 
@@ -223,7 +242,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_kernel(
   const elt* Vh = v + (int64_t)tc.bh * N * D;
   const elt* Gh = dout + (int64_t)tc.bh * M * D;
   const float* Lh = lse + (int64_t)tc.bh * M;
-  const float* Dh = delta + (int64_t)tc.bh * M;
+  const float* Dh = delta + (int64_t)tc.bh * M;  // -Delta per row (the workspace's first half)
   elt* dKh = dk + (int64_t)tc.bh * N * D;
   elt* dVh = dv + (int64_t)tc.bh * N * D;
 
@@ -260,7 +279,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_kernel(
       // Rows past M (and rows with no visible key, LSE = -inf) are masked before
       // their statistics are used; keep them finite here.
       float x = 0.0f;
-      if (r < M) x = tid < BQ ? Lh[r] * LOG2E : Dh[r];
+      if (r < M) x = tid < BQ ? Lh[r] * LOG2E : -Dh[r];
       st_val = (x == -INFINITY) ? 0.0f : x;
     }
   };
@@ -360,6 +379,365 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dK and dV on the fast path (fp16/bf16, D in {64, 96, 128}).
+//
+// The work split of fa_bwd_dkdv_kernel (4 waves of 32 keys, K and V rows in
+// registers, dK^T and dV^T accumulated over 64-query tiles), with:
+//  * Q, dO, L and Delta of a query tile copied HBM -> LDS directly
+//    (global_load_lds) into one of NBUF rotating buffers, NBUF - 2 query tiles
+//    ahead; the tiles use the forward's K-tile swizzle, which keeps both the
+//    row reads and the transposing reads free of bank conflicts.
+//  * A two-stage pipeline over 32-query halves u: while the MFMA unit computes
+//    S and dP of half u+1, the VALU forms dS of half u and rounds P and dS to
+//    16 bits; while it computes dV and dK of half u, the VALU exponentiates the
+//    scores of half u+1.
+//  * One barrier per query tile, between its two halves.  Waves do not skip
+//    halves that none of their keys sees: such a half is computed and masked
+//    to zero, which costs nothing since the wave would wait at the barrier.
+
+// The direct-to-LDS copy through inline assembly.  The compiler does not track
+// it, so it adds no conservative wait before LDS reads of other buffers; the
+// kernel owns every s_waitcnt vmcnt and barrier that orders a copy against its
+// readers.  M0 holds the LDS address of the copy (one wait state before the
+// load reads it) and is restored afterwards.  Lane l writes bytes
+// [16 l, 16 l + 16) (x4) or [4 l, 4 l + 4) (dword) after that address.
+__device__ __forceinline__ void lds_copy16(const void* g, unsigned lds_addr) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_addr)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_copy4(const void* g, unsigned lds_addr) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_addr)
+      : "memory");
+}
+
+template <class T, int DP, int NBUF>
+__global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
+    const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
+    const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dk,
+    typename T::elt* __restrict__ dv, int M, int N, int ktiles, float c, float scale, int causal) {
+  // lse is unused here: `delta` points at the workspace [2, B*H*M], whose
+  // second half holds -L / scale per row (see fa_bwd_delta_kernel).
+  using elt = typename T::elt;
+  using vec8 = typename T::vec8;
+  using L = FastLayout<DP>;
+  constexpr int D = DP;
+  constexpr int KK = DP / 16;
+  constexpr int DT = DP / 32;
+  constexpr int NW = BT / 64;
+  constexpr int BPW = L::NBLK / NW;  // 1 KB copies per wave per 64-row tile
+  constexpr int TB = L::TILEB;       // bytes of one 64-row tile
+  constexpr int BUFB = 2 * TB;       // Q and dO tiles of one query tile
+  constexpr int STB = 2 * BQ * 4;    // L and Delta of one query tile
+  constexpr int VMT = 2 * BPW + 1;   // copy instructions per wave per query tile
+  constexpr int BSTEP = NW * L::RPB; // rows between a lane's consecutive copies
+  static_assert(L::NBLK % NW == 0 && BSTEP % 16 == 0, "copy plan");
+  static_assert(NBUF == 3 || NBUF == 4, "pipeline depth");
+  static_assert(VMT < 16 && 2 * VMT < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * (BUFB + STB)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<false, BK>(ktiles);
+  const int k0 = tc.q0;
+  const elt* Qh = q + (int64_t)tc.bh * M * D;
+  const elt* Kh = k + (int64_t)tc.bh * N * D;
+  const elt* Vh = v + (int64_t)tc.bh * N * D;
+  const elt* Gh = dout + (int64_t)tc.bh * M * D;
+  const int64_t nrows = (int64_t)(gridDim.x / ktiles) * M;  // B*H*M
+  const float* Sh = delta + nrows + (int64_t)tc.bh * M;     // -L / scale per row
+  const float* Dh = delta + (int64_t)tc.bh * M;             // -Delta per row
+  elt* dKh = dk + (int64_t)tc.bh * N * D;
+  elt* dVh = dv + (int64_t)tc.bh * N * D;
+  (void)lse;
+
+  // Key j visible to query i iff j <= i + off; without the mask off = N (no
+  // query reaches it, so only the N tail is masked).
+  const int off = causal ? N - M : N;
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + l32;
+
+  vec8 kb[KK], vb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    kb[kk] = load_row8<T, true>(Kh, key, N, D, 16 * kk + 8 * h);
+    vb[kk] = load_row8<T, true>(Vh, key, N, D, 16 * kk + 8 * h);
+  }
+  f32x16 dka[DT], dva[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dka[dt] = f32x16{};
+    dva[dt] = f32x16{};
+  }
+
+  // Query tiles from the one holding the first query that sees key k0.
+  const int qt0 = max(0, k0 - off) / BQ;
+  const int nqt = (M + BQ - 1) / BQ;
+
+  // Copy plan (the forward's): wave w issues the 1 KB copies w + NW*i of each
+  // tile; lane l fills slot l % SLOTS of row (w + NW*i)*RPB + l / SLOTS.  Rows
+  // past M copy row M - 1 (their P is masked to 0).  Row statistics: wave w
+  // copies rows 32*(w % 2) .. +31 of -L/scale (w < 2) or -Delta (w >= 2), one
+  // dword per lane.
+  const int cp_sub = lane / L::SLOTS;
+  const int cp_slot = lane % L::SLOTS;
+  const int cp_row = w * L::RPB + cp_sub;
+  const int chunk = cp_slot ^ L::swz_k(cp_row);
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  const unsigned lds_w = __builtin_amdgcn_readfirstlane(lds0 + (unsigned)w * 1024u);
+  const unsigned lds_st =
+      __builtin_amdgcn_readfirstlane(lds0 + NBUF * BUFB + (unsigned)(w >> 1) * (BQ * 4));
+  const float* st_src = (w >> 1) ? Dh : Sh;
+  auto issue = [&](int qt) {
+    const int b = qt % NBUF;
+    const int q0 = qt * BQ;
+    const unsigned dst = lds_w + (unsigned)(b * BUFB);
+    if (chunk < L::CPR) {  // D = 96: slots 12..15 of a row hold no data
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int row = min(q0 + cp_row + i * BSTEP, M - 1);
+        const int64_t src = (int64_t)row * D + 8 * chunk;
+        lds_copy16(Qh + src, dst + NW * 1024 * i);
+        lds_copy16(Gh + src, dst + TB + NW * 1024 * i);
+      }
+    }
+    if (h == (w & 1)) lds_copy4(st_src + min(q0 + lane, M - 1), lds_st + (unsigned)(b * STB));
+  };
+  auto wait_copies = [&](int pending_tiles) {  // all but the last `pending_tiles` tiles landed
+    if (pending_tiles <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (pending_tiles == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMT) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * VMT) : "memory");
+  };
+  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // Row reads (A operands of S and dP, query rows in swap-2-3 order).
+  const int krow = swap23(l32);
+  int koff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * L::ROWB + 16 * ((2 * kk + h) ^ L::swz_k(krow));
+  // Transposing reads (A operands of dV^T and dK^T): lane j of a 16-lane group
+  // addresses row 8h + j/4 (+4 for the second read) of a 16-query chunk and 4
+  // features at 32dt + 16*dhalf + 4*(j%4); the swizzle repeats every 16 rows.
+  const int dhalf = (lane >> 4) & 1;
+  const int j16 = lane & 15;
+  int toff[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 8 * h + (j16 >> 2) + 4 * hi;
+      const int ch = 4 * dt + 2 * dhalf + ((j16 & 3) >> 1);
+      toff[dt][hi] = row * L::ROWB + 16 * (ch ^ L::swz_k(row)) + 8 * (j16 & 1);
+    }
+
+  // Row statistics (which = 0: -L/scale, 1: -Delta) of half t of buffer b in
+  // the accumulator order (register r <-> query 16 (r >> 3) + 8h + (r & 7)):
+  // the initial value of the S or dP accumulator.
+  auto read_stats = [&](int b, int which, int t, f32x16& x) {
+    const char* base = lds + NBUF * BUFB + b * STB + which * (BQ * 4) + 4 * (32 * t + 8 * h);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 y = *reinterpret_cast<const f32x4*>(base + 16 * ((g & 1) + 4 * (g >> 1)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * g + e] = y[e];
+    }
+  };
+
+  f32x16 p;         // P of the current half (masked)
+  f32x16 dpA, dpB;  // dP of the current / next half, alternating roles
+
+  // One pipeline step: CUR = dS, dV, dK of half (bc, tcur) from p and dp_cur
+  // (which holds dP - Delta); NEXT = S - L/scale, dP - Delta (into dp_next) and
+  // P (into p) of half (bn, tn).
+  //
+  // With both, the step is issued in a fixed order, one chunk per MFMA with
+  // scheduling fences between chunks: stage 1 runs the 2*KK S / dP MFMAs (row
+  // reads issued LA1 MFMAs ahead) beside the VALU work of dS and the 16-bit
+  // rounding of P and dS; stage 2 runs the 4*DT dV / dK MFMAs (transposing
+  // reads issued LA2 MFMAs ahead, the first ones during stage 1) beside the
+  // exponentials of the next half.
+  auto row_read = [&](int b, int t, int m) -> vec8 {  // A operand of stage-1 MFMA m
+    const char* base = lds + b * BUFB + 32 * t * L::ROWB + ((m & 1) ? TB : 0);
+    return *reinterpret_cast<const vec8*>(base + koff[m >> 1]);
+  };
+  auto tr_read = [&](int b, int t, int m) -> vec8 {  // A operand of stage-2 MFMA m
+    const int t2 = m / (2 * DT), dt = (m >> 1) % DT;
+    const char* base = lds + b * BUFB + 32 * t * L::ROWB + 16 * t2 * L::ROWB + ((m & 1) ? 0 : TB);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + toff[dt][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + toff[dt][1]));
+    return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto step = [&](auto cur_tag, auto next_tag, int bc, int tcur, int bn, int tn, f32x16& dp_cur,
+                  f32x16& dp_next) {
+    constexpr bool CUR = decltype(cur_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr int NM1 = 2 * KK, NM2 = 4 * DT;
+    f32x16 s;
+    vec8 pb[2], dsb[2];
+    if constexpr (CUR && NEXT) {
+      f32x16 ds;
+      vec8 ra[NM1], ta[NM2];
+      read_stats(bn, 0, tn, s);
+      read_stats(bn, 1, tn, dp_next);
+#pragma unroll
+      for (int m = 0; m < DKDV_LA1; ++m) ra[m] = row_read(bn, tn, m);
+      // Stage 1.  VALU units: 16 products dS = P * (dP - Delta), then the
+      // rounding of P (units 16, 17) and dS (18, 19).
+#pragma unroll
+      for (int m = 0; m < NM1; ++m) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (m + DKDV_LA1 < NM1) ra[m + DKDV_LA1] = row_read(bn, tn, m + DKDV_LA1);
+        const int pre = m - (NM1 - DKDV_LA2);  // first stage-2 reads, spread over the last MFMAs
+        if (pre >= 0) ta[pre] = tr_read(bc, tcur, pre);
+        if (m & 1) dp_next = T::mfma(ra[m], vb[m >> 1], dp_next);
+        else s = T::mfma(ra[m], kb[m >> 1], s);
+#pragma unroll
+        for (int u = 20 * m / NM1; u < 20 * (m + 1) / NM1; ++u) {
+          if (u < 16) {
+            float x = p[u] * dp_cur[u];
+            pin(x);
+            ds[u] = x;
+          } else {
+            f32x8 f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = u < 18 ? p[8 * (u & 1) + e] : ds[8 * (u & 1) + e];
+            vec8 y = __builtin_convertvector(f, vec8);
+            pin(y);
+            if (u < 18) pb[u & 1] = y;
+            else dsb[u & 1] = y;
+          }
+        }
+      }
+      // Stage 2.  VALU units: the 16 exponentials of the next half.
+#pragma unroll
+      for (int m = 0; m < NM2; ++m) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (m + DKDV_LA2 < NM2) ta[m + DKDV_LA2] = tr_read(bc, tcur, m + DKDV_LA2);
+        const int t2 = m / (2 * DT), dt = (m >> 1) % DT;
+        if (m & 1) dka[dt] = T::mfma(ta[m], dsb[t2], dka[dt]);
+        else dva[dt] = T::mfma(ta[m], pb[t2], dva[dt]);
+#pragma unroll
+        for (int r = 16 * m / NM2; r < 16 * (m + 1) / NM2; ++r) {
+          float x = __builtin_amdgcn_exp2f(s[r] * c);
+          pin(x);
+          p[r] = x;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // Pipeline head (S, dP, P only) or tail (dS, dV, dK only).
+      if (NEXT) {
+        read_stats(bn, 0, tn, s);
+        read_stats(bn, 1, tn, dp_next);
+#pragma unroll
+        for (int m = 0; m < NM1; ++m) {
+          const vec8 a = row_read(bn, tn, m);
+          if (m & 1) dp_next = T::mfma(a, vb[m >> 1], dp_next);
+          else s = T::mfma(a, kb[m >> 1], s);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] * c);
+      }
+      if (CUR) {
+        f32x16 ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = p[r] * dp_cur[r];
+        pack16<T>(p, pb);
+        pack16<T>(ds, dsb);
+#pragma unroll
+        for (int m = 0; m < NM2; ++m) {
+          const int t2 = m / (2 * DT), dt = (m >> 1) % DT;
+          const vec8 a = tr_read(bc, tcur, m);
+          if (m & 1) dka[dt] = T::mfma(a, dsb[t2], dka[dt]);
+          else dva[dt] = T::mfma(a, pb[t2], dva[dt]);
+        }
+      }
+    }
+#if defined(__HIP_DEVICE_COMPILE__)
+    // Keep P's exponentials in this step: without the use below they would be
+    // sunk past the mask's branch, away from the MFMAs they should overlap.
+    if (NEXT) asm volatile("" ::"v"(p));
+#endif
+  };
+
+  // Zero P where query qb + key_of_reg(r, h) does not see this lane's key
+  // (causal mask, M and N tails); rows with L = -inf are always masked here.
+  auto mask = [&](int u) {
+    const int qb = 32 * u;
+    if (qb + 31 >= M || kw0 + 31 >= N || kw0 + 31 > qb + off) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = qb + key_of_reg(r, h);
+        p[r] = (qi < M && key < N && key <= qi + off) ? p[r] : 0.0f;
+      }
+    }
+  };
+
+  using F = std::integral_constant<bool, false>;
+  using Tr = std::integral_constant<bool, true>;
+  if (qt0 < nqt) {
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+      if (qt0 + i < nqt) issue(qt0 + i);
+    wait_copies(min(NBUF - 2, nqt - 1 - qt0));
+    barrier();
+    step(F{}, Tr{}, 0, 0, qt0 % NBUF, 0, dpB, dpA);
+    mask(2 * qt0);
+    int b = qt0 % NBUF;
+    for (int j = qt0; j < nqt - 1; ++j) {
+      const int bn = b + 1 == NBUF ? 0 : b + 1;
+      step(Tr{}, Tr{}, b, 0, b, 1, dpA, dpB);
+      mask(2 * j + 1);
+      wait_copies(min(NBUF - 3, nqt - 2 - j));
+      barrier();
+      if (j + NBUF - 1 < nqt) issue(j + NBUF - 1);
+      step(Tr{}, Tr{}, b, 1, bn, 0, dpB, dpA);
+      mask(2 * j + 2);
+      b = bn;
+    }
+    // Last query tile: its second half has no successor.
+    step(Tr{}, Tr{}, b, 0, b, 1, dpA, dpB);
+    mask(2 * nqt - 1);
+    step(Tr{}, F{}, b, 1, 0, 0, dpB, dpA);
+  }
+
+  // Accumulator register 4g + e of tile dt holds feature 32dt + 8g + 4h + e of
+  // this lane's key.
+  if (key < N) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        store_row4<T, true>(dVh, key, D, d0, dva[dt], g, 1.0f);
+        store_row4<T, true>(dKh, key, D, d0, dka[dt], g, scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ.  DP: head dim padded to a multiple of 32; DFULL: D == DP.
 template <class T, int DP, bool CAUSAL, bool DFULL>
 __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
@@ -390,7 +768,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
   const elt* Vh = v + (int64_t)tc.bh * N * D;
   const elt* Gh = dout + (int64_t)tc.bh * M * D;
   const float* Lh = lse + (int64_t)tc.bh * M;
-  const float* Dh = delta + (int64_t)tc.bh * M;
+  const float* Dh = delta + (int64_t)tc.bh * M;  // -Delta per row (the workspace's first half)
   elt* dQh = dq + (int64_t)tc.bh * M * D;
 
   const int off = N - M;
@@ -413,7 +791,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
   float l2 = 0.0f, dl = 0.0f;
   if (qrow < M) {
     l2 = Lh[qrow] * LOG2E;
-    dl = Dh[qrow];
+    dl = -Dh[qrow];
   }
   if (l2 == -INFINITY) l2 = 0.0f;  // no visible key: every score of the row is masked
   f32x16 dqa[DT];
@@ -536,7 +914,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
   const elt* Vh = v + (int64_t)tc.bh * N * D;
   const elt* Gh = dout + (int64_t)tc.bh * M * D;
   const float* Lh = lse + (int64_t)tc.bh * M;
-  const float* Dh = delta + (int64_t)tc.bh * M;
+  const float* Dh = delta + (int64_t)tc.bh * M;  // -Delta per row (the workspace's first half)
   elt* dQh = dq + (int64_t)tc.bh * M * D;
 
   // Causal: key j visible to row i iff j <= i + off; without the mask `off` = N
@@ -561,7 +939,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
   float l2 = 0.0f, dl = 0.0f;
   if (qrow < M) {
     l2 = Lh[qrow] * LOG2E;
-    dl = Dh[qrow];
+    dl = -Dh[qrow];
   }
   if (l2 == -INFINITY) l2 = 0.0f;  // no visible key: every score of the row is masked
   f32x16 dqa[DT];
@@ -711,10 +1089,22 @@ void launch_bwd_tiles(const BwdArgs& a) {
   using elt = typename T::elt;
   if (a.N > 0) {
     const int ktiles = (a.N + BK - 1) / BK;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, DP, CAUSAL, DFULL>), dim3((unsigned)(a.BH * ktiles)),
-                       dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
-                       (const elt*)a.dout, a.lse, a.delta, (elt*)a.dk, (elt*)a.dv, a.M, a.N, a.D,
-                       ktiles, a.c, a.scale);
+    bool done = false;
+    if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
+      if (a.M > 0) {
+        hipLaunchKernelGGL((fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>),
+                           dim3((unsigned)(a.BH * ktiles)), dim3(BT), 0, a.stream,
+                           (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (const elt*)a.dout,
+                           a.lse, a.delta, (elt*)a.dk, (elt*)a.dv, a.M, a.N, ktiles, a.c, a.scale,
+                           CAUSAL ? 1 : 0);
+        done = true;
+      }
+    }
+    if (!done)
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, DP, CAUSAL, DFULL>), dim3((unsigned)(a.BH * ktiles)),
+                         dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
+                         (const elt*)a.dout, a.lse, a.delta, (elt*)a.dk, (elt*)a.dv, a.M, a.N, a.D,
+                         ktiles, a.c, a.scale);
   }
   if (a.M > 0) {
     if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
@@ -749,7 +1139,7 @@ void dispatch_bwd(const BwdArgs& a) {
     const int64_t blocks = (rows + 15) / 16;
     hipLaunchKernelGGL((fa_bwd_delta_kernel<T>), dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
                        dim3(BT), 0, a.stream, (const typename T::elt*)a.o,
-                       (const typename T::elt*)a.dout, a.delta, rows, a.D);
+                       (const typename T::elt*)a.dout, a.lse, a.delta, rows, a.D, a.scale);
   }
   if (a.D <= 32) dispatch_full<T, 32, CAUSAL>(a);
   else if (a.D <= 64) dispatch_full<T, 64, CAUSAL>(a);

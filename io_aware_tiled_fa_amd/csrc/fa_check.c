@@ -107,4 +107,4 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_abi_version(void) { return 3; }
+int fa_abi_version(void) { return 4; }

@@ -122,6 +122,19 @@ struct FastLayout {
 };
 
 
+// Pins a value at this point of the instruction stream: an empty statement
+// that reads and rewrites it, so the arithmetic producing it cannot be moved
+// past a later scheduling fence (device pass only; the host pass has no
+// vector registers).
+template <class X>
+__device__ __forceinline__ void pin(X& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#else
+  (void)x;
+#endif
+}
+
 __device__ __forceinline__ void copy16_to_lds(const void* g, char* lds_block) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
                                    (void __attribute__((address_space(3)))*)lds_block, 16, 0, 0);

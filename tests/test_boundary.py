@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
                           "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
 
 
 def test_status_strings():

@@ -83,6 +83,10 @@ SMALL = [
     _wl("bwd_m1_bf16", 1, 1, 1, 300, 64, "bf16", False, 3111),
     _wl("bwd_n1_f16", 1, 1, 300, 1, 64, "f16", False, 3112),
     _wl("bwd_empty_rows_f16", 1, 2, 300, 100, 64, "f16", True, 3113),
+    # fast dK/dV path: ragged query and key tails, M > N causal, many query tiles
+    _wl("bwd_fast_d128_ragged_bf16", 1, 2, 337, 261, 128, "bf16", False, 3114),
+    _wl("bwd_fast_d96_causal_mgtn_f16", 1, 1, 700, 450, 96, "f16", True, 3115),
+    _wl("bwd_fast_d64_many_tiles_bf16", 1, 1, 1100, 1030, 64, "bf16", True, 3116),
 ]
 
 
