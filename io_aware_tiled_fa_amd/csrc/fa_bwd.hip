@@ -427,6 +427,58 @@ __device__ __forceinline__ void lds_copy4(const void* g, unsigned lds_addr) {
       : "memory");
 }
 
+// The 2*NB direct-to-LDS copies of one query tile in one statement: for copy
+// i, NB-row blocks of Q (base qb) and dO (base gb) at the lane's byte offset
+// off[i] go to LDS addresses m0 + i*STRIDE and m0 + i*STRIDE + GOFF.  M0 is
+// saved once, stepped between copies (one wait state after each write) and
+// restored at the end.
+template <int NB, int STRIDE, int GOFF>
+__device__ __forceinline__ void lds_copy_tile(const void* qb, const void* gb, const unsigned (&off)[NB],
+                                              unsigned m0) {
+  unsigned saved;
+  if constexpr (NB == 4) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %2\n\t"
+        "s_add_u32 m0, m0, %8\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %3\n\t"
+        "s_add_u32 m0, m0, %9\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %2\n\t"
+        "s_add_u32 m0, m0, %8\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %3\n\t"
+        "s_add_u32 m0, m0, %9\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, %2\n\t"
+        "s_add_u32 m0, m0, %8\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %6, %3\n\t"
+        "s_add_u32 m0, m0, %9\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, %2\n\t"
+        "s_add_u32 m0, m0, %8\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %7, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0), "s"(qb), "s"(gb), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]),
+          "i"(GOFF), "i"(STRIDE - GOFF)
+        : "memory", "scc");
+  } else {
+    static_assert(NB == 2, "copies per wave");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %2\n\t"
+        "s_add_u32 m0, m0, %6\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %3\n\t"
+        "s_add_u32 m0, m0, %7\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %2\n\t"
+        "s_add_u32 m0, m0, %6\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0), "s"(qb), "s"(gb), "v"(off[0]), "v"(off[1]), "i"(GOFF), "i"(STRIDE - GOFF)
+        : "memory", "scc");
+  }
+}
+
 template <class T, int DP, int NBUF>
 __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
@@ -480,11 +532,6 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
   const int key = kw0 + l32;
 
   vec8 kb[KK], vb[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    kb[kk] = load_row8<T, true>(Kh, key, N, D, 16 * kk + 8 * h);
-    vb[kk] = load_row8<T, true>(Vh, key, N, D, 16 * kk + 8 * h);
-  }
   f32x16 dka[DT], dva[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -515,13 +562,18 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     const int q0 = qt * BQ;
     const unsigned dst = lds_w + (unsigned)(b * BUFB);
     if (chunk < L::CPR) {  // D = 96: slots 12..15 of a row hold no data
+      // Byte offsets within the head (M * D < 2^31 elements, so they fit 32 bits).
+      unsigned off[BPW];
+      const unsigned off0 = (unsigned)((q0 + cp_row) * D * 2 + 16 * chunk);
+      if (q0 + BQ <= M) {
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        const int row = min(q0 + cp_row + i * BSTEP, M - 1);
-        const int64_t src = (int64_t)row * D + 8 * chunk;
-        lds_copy16(Qh + src, dst + NW * 1024 * i);
-        lds_copy16(Gh + src, dst + TB + NW * 1024 * i);
+        for (int i = 0; i < BPW; ++i) off[i] = off0 + (unsigned)(i * BSTEP * D * 2);
+      } else {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i)
+          off[i] = (unsigned)(min(q0 + cp_row + i * BSTEP, M - 1) * D * 2 + 16 * chunk);
       }
+      lds_copy_tile<BPW, NW * 1024, TB>(Qh, Gh, off, dst);
     }
     if (h == (w & 1)) lds_copy4(st_src + min(q0 + lane, M - 1), lds_st + (unsigned)(b * STB));
   };
@@ -697,10 +749,17 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
 
   using F = std::integral_constant<bool, false>;
   using Tr = std::integral_constant<bool, true>;
-  if (qt0 < nqt) {
+  // The first copies go out before the K and V loads, so that their latencies
+  // overlap.
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
-      if (qt0 + i < nqt) issue(qt0 + i);
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (qt0 + i < nqt) issue(qt0 + i);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    kb[kk] = load_row8<T, true>(Kh, key, N, D, 16 * kk + 8 * h);
+    vb[kk] = load_row8<T, true>(Vh, key, N, D, 16 * kk + 8 * h);
+  }
+  if (qt0 < nqt) {
     wait_copies(min(NBUF - 2, nqt - 1 - qt0));
     barrier();
     step(F{}, Tr{}, 0, 0, qt0 % NBUF, 0, dpB, dpA);
