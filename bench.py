@@ -154,6 +154,11 @@ def main():
     ap.add_argument("--splits", type=int, default=0,
                     help="forward only: time fa_fwd_splitkv with this many key chunks "
                          "(0: plain fa_fwd, the headline path)")
+    ap.add_argument("--seq", type=int, default=0, metavar="S",
+                    help="measurement sweeps: run the workload with M = N = S (the driver's "
+                         "line uses the workload's own sizes)")
+    ap.add_argument("--batch", type=int, default=0, metavar="B",
+                    help="measurement sweeps: run the workload with this batch size")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of attention, run a plain device-to-device copy of BYTES "
                          "(3 times); used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -184,6 +189,11 @@ def main():
         return
     fa.load()
     w = WORKLOADS[args.workload]
+    if args.seq or args.batch:
+        B = args.batch or w.B
+        M = args.seq or w.M
+        N = args.seq or w.N
+        w = w.with_(name=f"{w.name}_B{B}_M{M}_N{N}", B=B, M=M, N=N)
     if args.which == "bwd":
         return bench_bwd(args, w)
     dev = torch.device("cuda:0")

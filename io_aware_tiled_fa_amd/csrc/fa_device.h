@@ -75,6 +75,40 @@ __device__ __forceinline__ TileCoord tile_coord(int qtiles) {
   return c;
 }
 
+// Persistent schedule.  A launch of P = gridDim.x workgroups covers `items`
+// work items (P <= items).  The items are cut into NXCD contiguous ranges, one
+// per XCD (workgroup g runs on XCD g % NXCD, so an XCD's L2 keeps its heads'
+// K and V), and the Px workgroups of an XCD take that range in rounds of Px,
+// in snake order: workgroup j takes index j in even rounds and Px - 1 - j in
+// odd ones, so that with heavy-first items each workgroup alternates heavy
+// and light ones.  Returns the item of `round`, or -1 once the range is done.
+// With P == items every workgroup takes exactly the item tile_coord gives it.
+__device__ __forceinline__ int persistent_item(int round, int items) {
+  const int P = gridDim.x;
+  const int g = blockIdx.x;
+  const int x = g % NXCD;
+  const int j = g / NXCD;
+  const int Px = P / NXCD + (x < P % NXCD ? 1 : 0);
+  const int per = items / NXCD;
+  const int rem = items % NXCD;
+  const int cnt = per + (x < rem ? 1 : 0);
+  const int jj = (round & 1) ? Px - 1 - j : j;
+  const int idx = round * Px + jj;
+  return idx < cnt ? x * per + min(x, rem) + idx : -1;
+}
+
+// (batch*head, first query row) of work item t: heads in order, and within a
+// head the query tiles heaviest-first under the causal mask.
+template <bool CAUSAL, int ROWS>
+__device__ __forceinline__ TileCoord item_coord(int t, int qtiles) {
+  TileCoord c;
+  c.bh = t / qtiles;
+  int qt = t - c.bh * qtiles;
+  if (CAUSAL) qt = qtiles - 1 - qt;
+  c.q0 = qt * ROWS;
+  return c;
+}
+
 // Lanes l and l^32 hold the same query row (different keys).  v_permlane32_swap
 // exchanges the two wave halves in one VALU op (no LDS round trip).
 __device__ __forceinline__ float pair_max(float x) {

@@ -404,7 +404,7 @@ template <class T, int DP, int NW, class OUT>
 __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, OUT* __restrict__ o, float* __restrict__ lse, int M,
-    int Ntot, int off_all, int qtiles, float c, KeySplit ks) {
+    int Ntot, int off_all, int qtiles, int items, float c, KeySplit ks) {
   constexpr bool CAUSAL = true;  // masking logic always on; `off` decides what it masks
   constexpr int D = DP;          // the dispatcher routes only D == DP here
   using elt = typename T::elt;
@@ -427,7 +427,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const TileCoord tc = tile_coord<CAUSAL, ROWS>(qtiles);
+  // Persistent loop (8-wave instantiations, one workgroup per CU): with fewer
+  // workgroups than work items a workgroup takes several items, one after the
+  // other, and the next item starts while the previous one's output stores
+  // drain.  The 4-wave instantiations (two workgroups per CU) run one item.
+  constexpr bool PERSIST = NW == 8;
+  for (int round = 0; PERSIST || round == 0; ++round) {
+  const int item = persistent_item(round, items);
+  if (item < 0) break;
+  const TileCoord tc = item_coord<CAUSAL, ROWS>(item, qtiles);
   const int q0 = tc.q0;
   const int nlo = (int)blockIdx.y * ks.chunk;  // first key of this launch's chunk
   const int N = min(ks.chunk, Ntot - nlo);     // keys in the chunk
@@ -630,6 +638,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     if (h == 0)
       Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
   }
+  }  // persistent loop
 }
 
 // ---------------------------------------------------------------------------
@@ -895,6 +904,29 @@ void launch_f32(const Launch& a) {
 template <int DP>
 constexpr int fast_waves() { return DP == 64 ? 4 : 8; }
 
+// Workgroup count for a persistent launch of `kernel` (with `threads` threads)
+// on the current device: one per CU when the occupancy calculator puts exactly
+// one workgroup on a CU, else 0 (launch one workgroup per item: co-resident
+// workgroups that start together stay in step and stop hiding each other's
+// prologue).  Cached per device; 0 too if the runtime cannot tell.
+template <class K>
+int persistent_workgroups(K kernel, int threads) {
+  static int cache[64];  // per device: -1 no, > 0 the count
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel),
+                                                     threads, 0) != hipSuccess)
+      return 0;
+    v = occ == 1 && cus > 0 ? cus : -1;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+  }
+  return v > 0 ? v : 0;
+}
+
 template <class T, int DP, bool CAUSAL>
 void launch_lp_fast(const Launch& a) {
   using elt = typename T::elt;
@@ -902,11 +934,15 @@ void launch_lp_fast(const Launch& a) {
   const int off = CAUSAL ? a.N - a.M : a.N;
   const int rows = 32 * NW;
   const int qtiles = (a.M + rows - 1) / rows;
-  const dim3 grid((unsigned)(a.BH * qtiles));
+  const int items = (int)(a.BH * qtiles);
+  // One workgroup per CU (persistent) where a workgroup fills a CU, else one
+  // per item.  Every XCD range needs a workgroup of its own: at least NXCD.
+  const int slots = persistent_workgroups(fa_fwd_lp_pipe_kernel<T, DP, NW, elt>, 64 * NW);
+  const int P = slots >= NXCD && slots < items ? slots : items;
   const KeySplit ks{a.N, 0, 0};
-  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, elt>), grid, dim3(64 * NW), 0, a.stream,
-                     (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M,
-                     a.N, off, qtiles, a.c, ks);
+  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, elt>), dim3((unsigned)P), dim3(64 * NW), 0,
+                     a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
+                     a.lse, a.M, a.N, off, qtiles, items, a.c, ks);
 }
 
 // Split-KV partials on the fast path (fp32 outputs into the workspace).
@@ -918,10 +954,11 @@ void launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, float* opa
   const int off = CAUSAL ? a.N - a.M : a.N;
   const int rows = 32 * NW;
   const int qtiles = (a.M + rows - 1) / rows;
-  const dim3 grid((unsigned)(a.BH * qtiles), (unsigned)G);
+  const int items = (int)(a.BH * qtiles);  // one workgroup per item and chunk
+  const dim3 grid((unsigned)items, (unsigned)G);
   hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, float>), grid, dim3(64 * NW), 0,
                      a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart,
-                     a.M, a.N, off, qtiles, a.c, ks);
+                     a.M, a.N, off, qtiles, items, a.c, ks);
 }
 
 template <class T, bool CAUSAL>
