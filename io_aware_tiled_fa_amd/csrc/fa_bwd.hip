@@ -484,7 +484,8 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dk,
-    typename T::elt* __restrict__ dv, int M, int N, int ktiles, float c, float scale, int causal) {
+    typename T::elt* __restrict__ dv, int M, int N, int ktiles, int items, float c, float scale,
+    int causal) {
   // lse is unused here: `delta` points at the workspace [2, B*H*M], whose
   // second half holds -L / scale per row (see fa_bwd_delta_kernel).
   using elt = typename T::elt;
@@ -512,13 +513,18 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const TileCoord tc = tile_coord<false, BK>(ktiles);
+  // Persistent loop at D >= 96 (one workgroup per CU): items are
+  // (batch*head, key tile), key tiles in natural order (under the causal mask
+  // the first see the most queries), taken in the snake order of
+  // persistent_item.  At D = 64 (two workgroups per CU) one item each.
+  constexpr bool PERSIST = DP >= 96;
+  auto work = [&](const TileCoord tc) {
   const int k0 = tc.q0;
   const elt* Qh = q + (int64_t)tc.bh * M * D;
   const elt* Kh = k + (int64_t)tc.bh * N * D;
   const elt* Vh = v + (int64_t)tc.bh * N * D;
   const elt* Gh = dout + (int64_t)tc.bh * M * D;
-  const int64_t nrows = (int64_t)(gridDim.x / ktiles) * M;  // B*H*M
+  const int64_t nrows = (int64_t)(items / ktiles) * M;  // B*H*M
   const float* Sh = delta + nrows + (int64_t)tc.bh * M;     // -L / scale per row
   const float* Dh = delta + (int64_t)tc.bh * M;             // -Delta per row
   elt* dKh = dk + (int64_t)tc.bh * N * D;
@@ -794,6 +800,20 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
         store_row4<T, true>(dKh, key, D, d0, dka[dt], g, scale);
       }
   }
+  };  // work
+
+  if constexpr (PERSIST) {
+    for (int round = 0;; ++round) {
+      const int item = persistent_item(round, items);
+      if (item < 0) break;
+      // The previous item's last reads of the LDS buffers precede this item's
+      // first copies into them.
+      if (round > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      work(item_coord<false, BK>(item, ktiles));
+    }
+  } else {
+    work(tile_coord<false, BK>(ktiles));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -944,7 +964,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dq,
-    int M, int N, int qtiles, float c, float scale, int causal) {
+    int M, int N, int qtiles, int items, float c, float scale, int causal) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using L = FastLayout<DP>;
@@ -966,7 +986,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const TileCoord tc = tile_coord<true, ROWS>(qtiles);  // heaviest causal tiles first
+  // Persistent loop for the 8-wave instantiations (one workgroup per CU), as in
+  // the forward's fast path; the 4-wave ones take one item per workgroup.
+  constexpr bool PERSIST = NW == 8;
+  for (int round = 0; PERSIST || round == 0; ++round) {
+  const int item = persistent_item(round, items);
+  if (item < 0) break;
+  const TileCoord tc = item_coord<true, ROWS>(item, qtiles);  // heaviest causal tiles first
   const int q0 = tc.q0;
   const elt* Qh = q + (int64_t)tc.bh * M * D;
   const elt* Kh = k + (int64_t)tc.bh * N * D;
@@ -1127,6 +1153,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
       for (int g = 0; g < 4; ++g)
         store_row4<T, true>(dQh, qrow, D, 32 * dt + 8 * g + 4 * h, dqa[dt], g, scale);
   }
+  }  // persistent loop
 }
 
 // ---------------------------------------------------------------------------
@@ -1151,11 +1178,13 @@ void launch_bwd_tiles(const BwdArgs& a) {
     bool done = false;
     if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
       if (a.M > 0) {
-        hipLaunchKernelGGL((fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>),
-                           dim3((unsigned)(a.BH * ktiles)), dim3(BT), 0, a.stream,
-                           (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (const elt*)a.dout,
-                           a.lse, a.delta, (elt*)a.dk, (elt*)a.dv, a.M, a.N, ktiles, a.c, a.scale,
-                           CAUSAL ? 1 : 0);
+        const int items = (int)(a.BH * ktiles);
+        const int slots = persistent_workgroups(fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>, BT);
+        const int P = slots >= NXCD && slots < items ? slots : items;
+        hipLaunchKernelGGL((fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>), dim3((unsigned)P),
+                           dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k,
+                           (const elt*)a.v, (const elt*)a.dout, a.lse, a.delta, (elt*)a.dk,
+                           (elt*)a.dv, a.M, a.N, ktiles, items, a.c, a.scale, CAUSAL ? 1 : 0);
         done = true;
       }
     }
@@ -1170,10 +1199,13 @@ void launch_bwd_tiles(const BwdArgs& a) {
       if (a.N > 0) {
         constexpr int NW = DP == 64 ? 4 : 8;
         const int qtiles = (a.M + 32 * NW - 1) / (32 * NW);
-        hipLaunchKernelGGL((fa_bwd_dq_fast_kernel<T, DP, NW>), dim3((unsigned)(a.BH * qtiles)),
-                           dim3(64 * NW), 0, a.stream, (const elt*)a.q, (const elt*)a.k,
-                           (const elt*)a.v, (const elt*)a.dout, a.lse, a.delta, (elt*)a.dq, a.M,
-                           a.N, qtiles, a.c, a.scale, CAUSAL ? 1 : 0);
+        const int items = (int)(a.BH * qtiles);
+        const int slots = persistent_workgroups(fa_bwd_dq_fast_kernel<T, DP, NW>, 64 * NW);
+        const int P = slots >= NXCD && slots < items ? slots : items;
+        hipLaunchKernelGGL((fa_bwd_dq_fast_kernel<T, DP, NW>), dim3((unsigned)P), dim3(64 * NW), 0,
+                           a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
+                           (const elt*)a.dout, a.lse, a.delta, (elt*)a.dq, a.M, a.N, qtiles, items,
+                           a.c, a.scale, CAUSAL ? 1 : 0);
         return;
       }
     }

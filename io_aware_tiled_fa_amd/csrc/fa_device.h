@@ -109,6 +109,29 @@ __device__ __forceinline__ TileCoord item_coord(int t, int qtiles) {
   return c;
 }
 
+// Workgroup count for a persistent launch of `kernel` (with `threads` threads)
+// on the current device: one per CU when the occupancy calculator puts exactly
+// one workgroup on a CU, else 0 (launch one workgroup per item: co-resident
+// workgroups that start together stay in step and stop hiding each other's
+// prologue).  Cached per device; 0 too if the runtime cannot tell.
+template <class K>
+int persistent_workgroups(K kernel, int threads) {
+  static int cache[64];  // per device: -1 no, > 0 the count
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel),
+                                                     threads, 0) != hipSuccess)
+      return 0;
+    v = occ == 1 && cus > 0 ? cus : -1;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+  }
+  return v > 0 ? v : 0;
+}
+
 // Lanes l and l^32 hold the same query row (different keys).  v_permlane32_swap
 // exchanges the two wave halves in one VALU op (no LDS round trip).
 __device__ __forceinline__ float pair_max(float x) {

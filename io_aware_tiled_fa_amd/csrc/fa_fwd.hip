@@ -904,29 +904,6 @@ void launch_f32(const Launch& a) {
 template <int DP>
 constexpr int fast_waves() { return DP == 64 ? 4 : 8; }
 
-// Workgroup count for a persistent launch of `kernel` (with `threads` threads)
-// on the current device: one per CU when the occupancy calculator puts exactly
-// one workgroup on a CU, else 0 (launch one workgroup per item: co-resident
-// workgroups that start together stay in step and stop hiding each other's
-// prologue).  Cached per device; 0 too if the runtime cannot tell.
-template <class K>
-int persistent_workgroups(K kernel, int threads) {
-  static int cache[64];  // per device: -1 no, > 0 the count
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-  if (v == 0) {
-    int cus = 0, occ = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel),
-                                                     threads, 0) != hipSuccess)
-      return 0;
-    v = occ == 1 && cus > 0 ? cus : -1;
-    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
-  }
-  return v > 0 ? v : 0;
-}
-
 template <class T, int DP, bool CAUSAL>
 void launch_lp_fast(const Launch& a) {
   using elt = typename T::elt;
