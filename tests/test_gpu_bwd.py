@@ -117,6 +117,18 @@ def test_bwd_stress_large_logits():
     _check_heads(w)
 
 
+@pytest.mark.parametrize("w", [
+    # more (head, tile) items than workgroups: the persistent dK/dV and dQ
+    # launches, with item counts that do not divide evenly over the XCDs
+    _wl("bwd_persistent_bf16_causal", 3, 27, 1024, 1024, 128, "bf16", True, 3121),
+    _wl("bwd_persistent_f16_d96", 2, 37, 500, 700, 96, "f16", False, 3122),
+], ids=lambda w: w.name)
+def test_bwd_persistent_launch(w):
+    _say(f"{w}")
+    nh = w.B * w.H
+    _check_heads(w, heads=sorted({0, 1, nh // 3, nh // 2, nh - 2, nh - 1}))
+
+
 def test_bwd_no_keys_and_no_queries():
     import torch
 

@@ -117,6 +117,20 @@ def test_stress_f16_all_rows(name):
     check(w.name, w.dtype, o.double().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref)
 
 
+def test_persistent_launch_all_rows():
+    """More (head, query tile) items than workgroups (persistent schedule),
+    with an item count (333) that does not divide evenly over the XCDs."""
+    from workloads import Workload
+
+    w = Workload(name="persistent_bf16_d128", B=3, H=37, M=600, N=600, D=128, dtype="bf16",
+                 causal=False, scale=1.0 / math.sqrt(128), seed=1101)
+    _say(f"{w}")
+    qc, kc, vc = make_inputs(w)
+    o, lse = _run(w, qc, kc, vc)
+    O_ref, L_ref = oracle.attention(_flat(qc), _flat(kc), _flat(vc), w.scale, w.causal)
+    check(w.name, w.dtype, _flat(o.double()).cpu().numpy(), _flat(lse).cpu().numpy(), O_ref, L_ref)
+
+
 def test_long_context_bf16_sampled():
     w = WORKLOADS["long_context_bf16"]
     _say(f"{w}")
