@@ -109,6 +109,19 @@ __device__ __forceinline__ TileCoord item_coord(int t, int qtiles) {
   return c;
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+inline int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
+
 // Workgroup count for a persistent launch of `kernel` (with `threads` threads)
 // on the current device: one per CU when the occupancy calculator puts exactly
 // one workgroup on a CU, else 0 (launch one workgroup per item: co-resident

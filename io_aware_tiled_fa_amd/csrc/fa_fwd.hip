@@ -904,10 +904,9 @@ void launch_f32(const Launch& a) {
 template <int DP>
 constexpr int fast_waves() { return DP == 64 ? 4 : 8; }
 
-template <class T, int DP, bool CAUSAL>
-void launch_lp_fast(const Launch& a) {
+template <class T, int DP, bool CAUSAL, int NW>
+void launch_lp_fast_nw(const Launch& a) {
   using elt = typename T::elt;
-  constexpr int NW = fast_waves<DP>();
   const int off = CAUSAL ? a.N - a.M : a.N;
   const int rows = 32 * NW;
   const int qtiles = (a.M + rows - 1) / rows;
@@ -920,6 +919,21 @@ void launch_lp_fast(const Launch& a) {
   hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, elt>), dim3((unsigned)P), dim3(64 * NW), 0,
                      a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
                      a.lse, a.M, a.N, off, qtiles, items, a.c, ks);
+}
+
+// At D = 96 and 128, when even 128-row workgroups (twice as many) leave a CU
+// for each, the grid runs on those: the same work on twice the CUs.  (Where
+// the doubled grid would put two workgroups on some CUs it measured slower.)
+template <class T, int DP, bool CAUSAL>
+void launch_lp_fast(const Launch& a) {
+  constexpr int NW = fast_waves<DP>();
+  if constexpr (NW == 8) {
+    const int64_t wide = a.BH * ((a.M + 32 * NW - 1) / (32 * NW));
+    const int cus = device_cus();
+    if (cus > 0 && a.BH * ((a.M + 127) / 128) <= cus && wide < cus)
+      return launch_lp_fast_nw<T, DP, CAUSAL, 4>(a);
+  }
+  launch_lp_fast_nw<T, DP, CAUSAL, NW>(a);
 }
 
 // Split-KV partials on the fast path (fp32 outputs into the workspace).
