@@ -19,6 +19,11 @@ stream the kernel runs on.  Peak: MI355X dense bf16/fp16 MFMA 2516.6 TFLOP/s
 The cpu_baseline object times the fp64 CPU oracle (untuned) on a bounded sample
 of the same workload (whole heads, all rows) on this host's cores.
 
+``--sdpa`` times PyTorch's own fused scaled_dot_product_attention (its flash or
+memory-efficient backend; never the math path) on the same inputs, as context
+only: another party's implementation, not a target.  Causal calls need M = N
+(PyTorch aligns its causal mask top-left).
+
 ``--pass bwd`` times fa_bwd instead (the forward runs once before the timed
 region and its O and LSE are inputs, as in training).  Its algorithmic work is
 the pages' count for a backward pass with recomputation, five products of
@@ -159,6 +164,9 @@ def main():
                          "line uses the workload's own sizes)")
     ap.add_argument("--batch", type=int, default=0, metavar="B",
                     help="measurement sweeps: run the workload with this batch size")
+    ap.add_argument("--sdpa", action="store_true",
+                    help="context only: time PyTorch's fused SDPA (flash / memory-efficient "
+                         "backend) on the same workload instead of fa_fwd")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of attention, run a plain device-to-device copy of BYTES "
                          "(3 times); used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -196,6 +204,8 @@ def main():
         w = w.with_(name=f"{w.name}_B{B}_M{M}_N{N}", B=B, M=M, N=N)
     if args.which == "bwd":
         return bench_bwd(args, w)
+    if args.sdpa:
+        return bench_sdpa(args, w)
     dev = torch.device("cuda:0")
     log(f"workload {w}")
     qc, kc, vc = make_inputs(w)
@@ -293,6 +303,71 @@ def main():
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, qc, kc, vc, budget_s=args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def bench_sdpa(args, w):
+    """Context: PyTorch's fused SDPA forward on the workload, timed like fa_fwd."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    import io_aware_tiled_fa_amd as fa
+
+    if w.dtype == "f32" or (w.causal and w.M != w.N):
+        print("--sdpa covers fp16/bf16 workloads, causal ones only with M = N (PyTorch aligns "
+              "its causal mask top-left)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    log(f"workload {w} (PyTorch SDPA, context)")
+    qc, kc, vc = make_inputs(w)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    backend = None
+    for b in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel(b):
+                o_ref = F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
+            torch.cuda.synchronize()
+            backend = b
+            break
+        except RuntimeError as e:  # backend not built for this GPU or shape: try the next
+            log(f"{b.name}: unavailable ({str(e).splitlines()[0][:120]})")
+    if backend is None:
+        print(json.dumps({"metric": "context: PyTorch SDPA forward", "value": None,
+                          "note": "no fused SDPA backend available", "torch": torch.__version__}))
+        return
+    o_fa, _ = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    diff = (o_fa.float() - o_ref.float()).abs().max().item()
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        with sdpa_kernel(backend):
+            F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(K):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / K
+    peak = PEAK_TFLOPS[w.dtype]
+    tflops = metric_flops(w.B, w.H, w.M, w.N, w.D, w.causal) / (ms * 1e-3) / 1e12
+    log(f"SDPA ({backend.name}) ms/step {ms:.4f}  {tflops:.1f} TFLOP/s  max|O_sdpa - O_fa_fwd| {diff:.3e}")
+    print(json.dumps({
+        "metric": "context: PyTorch SDPA forward TFLOP/s on the same workload (not a target)",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+        "pct_of_mfma_peak": round(100.0 * tflops / peak, 2), "steps": K, "warmup": args.warmup,
+        "backend": backend.name, "torch": torch.__version__,
+        "max_abs_diff_vs_fa_fwd": diff, "config": {"workload": w.name, "B": w.B, "H": w.H,
+                                                   "M": w.M, "N": w.N, "D": w.D,
+                                                   "causal": w.causal, "dtype": w.dtype},
+    }), flush=True)
 
 
 def bench_bwd(args, w):
