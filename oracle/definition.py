@@ -22,7 +22,7 @@ The log-sum-exp is the one number per row kept for the backward pass
 ("The backward pass: recompute instead of store" on the Module 08 page:
 L = m + log(l)).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * Causal alignment when M != N: the pages only show square masks (``np.tril`` /
   ``cols <= rows``).  Bottom-right alignment ``j <= i + N - M`` is used; it is
