@@ -296,6 +296,8 @@ def main():
                        "fa_fwd_f32_kernel" if w.dtype == "f32" else
                        "fa_fwd_lp_pipe_kernel" if w.D in (64, 96, 128) else "fa_fwd_lp_kernel"),
             "avg_launch_ms": round(avg_launch_ms, 5),
+            "median_launch_ms": round(med_launch_ms, 5),
+            "min_launch_ms": round(min(launch_ms), 5),
             "hbm_gbs_compulsory": round(compulsory_bytes(w) / (avg_launch_ms * 1e-3) / 1e9, 1),
         },
     }
