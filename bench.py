@@ -127,6 +127,17 @@ def cpu_baseline_bwd(w, qc, kc, vc, gc, budget_s: float = 15.0):
     }
 
 
+def f32_kernel(w):
+    """The fp32 kernel fa_fwd launches: the key-split one when D <= 64 and the
+    plain grid (128 query rows per workgroup) would fill under half the CUs."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = w.B * w.H * ((w.M + 127) // 128)
+    return "fa_fwd_f32_ksplit_kernel" if w.D <= 64 and w.N > 0 and 2 * grid < cus \
+        else "fa_fwd_f32_kernel"
+
+
 def load_traffic(w, kernel_ms):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they match."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -293,7 +304,7 @@ def main():
             "traffic": traffic,
             "kernel": (("fa_fwd_f32_kernel" if w.dtype == "f32" else "fa_fwd_lp_kernel")
                        + " + fa_merge_kernel (split-KV)" if args.splits else
-                       "fa_fwd_f32_kernel" if w.dtype == "f32" else
+                       f32_kernel(w) if w.dtype == "f32" else
                        "fa_fwd_lp_pipe_kernel" if w.D in (64, 96, 128) else "fa_fwd_lp_kernel"),
             "avg_launch_ms": round(avg_launch_ms, 5),
             "median_launch_ms": round(med_launch_ms, 5),

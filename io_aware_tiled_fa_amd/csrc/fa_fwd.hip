@@ -813,6 +813,216 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// fp32 forward for grids far too small to fill the GPU (D <= 64): the four
+// waves of a workgroup share its 32 query rows and split every 128-key step
+// between them (wave w takes keys 32w..32w+31 of the step), each running the
+// recurrence of fa_fwd_f32_kernel over its keys.  At the end the partial
+// results are combined through LDS by the concatenation algebra of "Module 08:
+// FlashAttention and Memory-Efficient Kernels" ("Tiling and the online
+// softmax"): with m = max_w m_w and a_w = 2^(m_w - m) (base-2 scaled units),
+//   l = sum_w a_w l_w,   O = sum_w a_w acc_w / l,   LSE = ln2 (m + log2 l).
+// A wave that saw no key has m_w = -inf and weight 0; a row that sees no key
+// at all keeps O = 0 and LSE = -inf.  Four times the workgroups of the plain
+// kernel for the same problem, each with a quarter of the keys.
+template <int DP, bool CAUSAL, bool DFULL>
+__global__ __launch_bounds__(NTHREADS, 1) void fa_fwd_f32_ksplit_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+  constexpr int ROWS = 32;
+  constexpr int KEYS = 4 * BN32;                // keys per step (all four waves)
+  constexpr int KSTR = DP + 1;
+  constexpr int VSTR = DP + 4;
+  constexpr int K_ELEMS = KEYS * KSTR;
+  constexpr int V_ELEMS = KEYS * VSTR;
+  constexpr int STAGE = K_ELEMS + V_ELEMS;
+  constexpr int CH = DP / 4;                    // 16-byte chunks per row
+  constexpr int LD = (KEYS * CH + NTHREADS - 1) / NTHREADS;
+  constexpr int DT = DP / 32;
+  constexpr int KS = DP / 2;                    // k-steps of S^T
+  static_assert(4 * ROWS * DP + 8 * ROWS <= 2 * STAGE, "merge buffers fit in the stages");
+
+  __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<CAUSAL, ROWS>(qtiles);
+  const int q0 = tc.q0;
+  const float* Qh = q + (int64_t)tc.bh * M * D;
+  const float* Kh = k + (int64_t)tc.bh * N * D;
+  const float* Vh = v + (int64_t)tc.bh * N * D;
+  float* Oh = o + (int64_t)tc.bh * M * D;
+  float* Lh = lse + (int64_t)tc.bh * M;
+
+  const int off = N - M;
+  const int qrow = q0 + l32;
+  const int q_last = min(q0 + ROWS - 1, M - 1);
+  // keys any row of the workgroup sees
+  const int w_end = CAUSAL ? min(N, q_last + 1 + off) : N;
+  const int ntiles = w_end > 0 ? (w_end + KEYS - 1) / KEYS : 0;
+  const int lim = CAUSAL ? min(N, qrow + off + 1) : N;
+
+  float qreg[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    const int d = 2 * st + h;
+    qreg[st] = (qrow < M && d < D) ? Qh[(int64_t)qrow * D + d] : 0.0f;
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  float4 kr[LD], vr[LD];
+  auto load_tile = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int ci = tid + NTHREADS * i;
+      const int row = ci / CH;
+      const int col = (ci - row * CH) * 4;
+      const int key = n0 + row;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (ci < KEYS * CH && key < N) {
+        if (DFULL) {
+          a = *reinterpret_cast<const float4*>(Kh + (int64_t)key * D + col);
+          b = *reinterpret_cast<const float4*>(Vh + (int64_t)key * D + col);
+        } else {
+          const float* kp = Kh + (int64_t)key * D;
+          const float* vp = Vh + (int64_t)key * D;
+          a.x = col + 0 < D ? kp[col + 0] : 0.f;
+          a.y = col + 1 < D ? kp[col + 1] : 0.f;
+          a.z = col + 2 < D ? kp[col + 2] : 0.f;
+          a.w = col + 3 < D ? kp[col + 3] : 0.f;
+          b.x = col + 0 < D ? vp[col + 0] : 0.f;
+          b.y = col + 1 < D ? vp[col + 1] : 0.f;
+          b.z = col + 2 < D ? vp[col + 2] : 0.f;
+          b.w = col + 3 < D ? vp[col + 3] : 0.f;
+        }
+      }
+      kr[i] = a;
+      vr[i] = b;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    float* Ks = smem + stage * STAGE;
+    float* Vs = Ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int ci = tid + NTHREADS * i;
+      if (ci < KEYS * CH) {
+        const int row = ci / CH;
+        const int col = (ci - row * CH) * 4;
+        float* kp = Ks + row * KSTR + col;
+        kp[0] = kr[i].x;
+        kp[1] = kr[i].y;
+        kp[2] = kr[i].z;
+        kp[3] = kr[i].w;
+        *reinterpret_cast<float4*>(Vs + row * VSTR + col) = vr[i];
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const int krow = swap23(l32);
+  for (int j = 0; j < ntiles; ++j) {
+    const int n0 = j * KEYS;
+    const bool more = j + 1 < ntiles;
+    if (more) load_tile(n0 + KEYS);
+    const int nw = n0 + BN32 * w;  // this wave's first key
+    if (nw < w_end) {
+      const float* Ks = smem + (j & 1) * STAGE + BN32 * w * KSTR;
+      const float* Vs = smem + (j & 1) * STAGE + K_ELEMS + BN32 * w * VSTR;
+      f32x16 s[1] = {f32x16{}};
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[krow * KSTR + 2 * st + h], qreg[st], s[0],
+                                                    0, 0, 0);
+      const bool need_mask = (nw + BN32 > N) || (CAUSAL && nw + BN32 - 1 > q0 + off);
+      if (need_mask) apply_mask<1>(s, nw, h, lim);
+      const SoftmaxStep st = softmax_update<1>(s, c, m_run, l_run);
+      if (st.rescale) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= st.alpha;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key_of_reg(r, h);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VSTR + 32 * dt + l32], s[0][r],
+                                                         acc[dt], 0, 0, 0);
+      }
+    }
+    if (more) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // Merge the four waves' partial results (the stage buffers are free now).
+  float* part = smem;                    // [4][ROWS][DP] accumulators, scaled by a_w
+  float* mst = smem + 4 * ROWS * DP;     // [4][ROWS] maxima
+  float* lst = mst + 4 * ROWS;           // [4][ROWS] sums
+  const float l_w = pair_sum(l_run);
+  if (h == 0) {
+    mst[w * ROWS + l32] = m_run;
+    lst[w * ROWS + l32] = l_w;
+  }
+  __syncthreads();
+  float m_all = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) m_all = fmaxf(m_all, mst[u * ROWS + l32]);
+  const float a_w = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_all);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 32 * dt + 8 * g + 4 * h + e;
+        part[(w * ROWS + l32) * DP + d] = acc[dt][4 * g + e] * a_w;
+      }
+  __syncthreads();
+  // Thread t combines row t / 8, features 8 (t % 8) .. + 7 (DP / 8 at a time).
+  {
+    constexpr int PER = DP / 8;
+    const int row = tid >> 3;
+    const int d0 = (tid & 7) * PER;
+    float mr = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mr = fmaxf(mr, mst[u * ROWS + row]);
+    float l_tot = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float mu = mst[u * ROWS + row];
+      l_tot += mu == -INFINITY ? 0.0f : lst[u * ROWS + row] * __builtin_amdgcn_exp2f(mu - mr);
+    }
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int grow = q0 + row;
+    if (grow < M) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int d = d0 + e;
+        const float y = (part[(0 * ROWS + row) * DP + d] + part[(1 * ROWS + row) * DP + d] +
+                         part[(2 * ROWS + row) * DP + d] + part[(3 * ROWS + row) * DP + d]) *
+                        inv;
+        if (DFULL || d < D) Oh[(int64_t)grow * D + d] = y;
+      }
+      if ((tid & 7) == 0)
+        Lh[grow] = l_tot > 0.0f ? LN2F * (mr + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of split-KV partial results: the concatenation algebra of "Module 08:
 // FlashAttention and Memory-Efficient Kernels" ("Tiling and the online
 // softmax": the softmax of a concatenation follows from the maxima and sums of
@@ -965,8 +1175,29 @@ void dispatch_lp(const Launch& a) {
   else launch_lp<T, 128, CAUSAL>(a);
 }
 
+// fp32 with D <= 64 on a grid that would leave most of the GPU idle: split
+// each workgroup's keys over its four waves (four times the workgroups).
+template <int DP, bool CAUSAL>
+void launch_f32_ksplit(const Launch& a) {
+  const int qtiles = (a.M + 31) / 32;
+  const dim3 grid((unsigned)(a.BH * qtiles));
+  if (a.D == DP)
+    hipLaunchKernelGGL((fa_fwd_f32_ksplit_kernel<DP, CAUSAL, true>), grid, dim3(NTHREADS), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.o, a.lse, a.M, a.N, a.D, qtiles, a.c);
+  else
+    hipLaunchKernelGGL((fa_fwd_f32_ksplit_kernel<DP, CAUSAL, false>), grid, dim3(NTHREADS), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.o, a.lse, a.M, a.N, a.D, qtiles, a.c);
+}
+
 template <bool CAUSAL>
 void dispatch_f32(const Launch& a) {
+  const int cus = device_cus();
+  if (!a.generic && a.N > 0 && a.D <= 64 && cus > 0 && 2 * (int64_t)a.grid.x < cus) {
+    if (a.D <= 32) return launch_f32_ksplit<32, CAUSAL>(a);
+    return launch_f32_ksplit<64, CAUSAL>(a);
+  }
   if (a.D <= 32) launch_f32<32, CAUSAL>(a);
   else if (a.D <= 64) launch_f32<64, CAUSAL>(a);
   else if (a.D <= 96) launch_f32<96, CAUSAL>(a);

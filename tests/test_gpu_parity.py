@@ -73,6 +73,21 @@ def test_f32_odd_shapes(M, N, D):
     check(f"f32_{M}x{N}x{D}", "f32", o.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref)
 
 
+@pytest.mark.parametrize("M,N,D", [(300, 700, 64), (257, 257, 40), (700, 300, 32)])
+def test_f32_small_grid_key_split(M, N, D):
+    """fp32 grids too small to fill the GPU run with the keys of each workgroup
+    split over its waves and merged at the end: causal (bottom-right), several
+    128-key steps with a ragged tail, full and padded D, and (M > N) rows that
+    see no key at all."""
+    w = WORKLOADS["single_head_f32"].with_(B=1, H=2, M=M, N=N, D=D, scale=1 / math.sqrt(D),
+                                           causal=True, seed=91)
+    _say(f"{w}")
+    qc, kc, vc = make_inputs(w)
+    o, lse = _run(w, qc, kc, vc)
+    O_ref, L_ref = oracle.attention(qc, kc, vc, w.scale, True)
+    check(f"f32_split_{M}x{N}x{D}", "f32", o.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref)
+
+
 def _sampled_check(w, o, lse, qc, kc, vc, rows_per_head, full_heads=()):
     import torch
 
