@@ -73,7 +73,8 @@ def test_f32_odd_shapes(M, N, D):
     check(f"f32_{M}x{N}x{D}", "f32", o.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref)
 
 
-@pytest.mark.parametrize("M,N,D", [(300, 700, 64), (257, 257, 40), (700, 300, 32)])
+@pytest.mark.parametrize("M,N,D", [(300, 700, 64), (257, 257, 40), (700, 300, 32), (1, 65536, 64),
+                                   (5, 1000, 1)])
 def test_f32_small_grid_key_split(M, N, D):
     """fp32 grids too small to fill the GPU run with the keys of each workgroup
     split over its waves and merged at the end: causal (bottom-right), several
