@@ -173,3 +173,33 @@ def test_bwd_sum_rules_and_determinism():
     dk_sum = dk.double().sum(dim=2).cpu()
     scale_dk = dk.double().abs().sum(dim=2).cpu().max().item()
     assert dk_sum.abs().max().item() <= 2e-2 * scale_dk + 1e-3
+
+
+def test_bwd_tensors_beyond_2_31_elements():
+    """Forward and backward with Q, K, V, dO and the gradients of more than 2^31
+    elements each (16385 heads of 1024 x 128, bf16, causal): every gradient of
+    the first head, the heads on either side of the 2^31-element offset and the
+    last head against the oracle.  Inputs are drawn on the GPU (seeded)."""
+    import torch
+    from workloads import make_dout_device, make_inputs_device
+
+    w = _wl("bwd_big_bf16_causal", 1, 16385, 1024, 1024, 128, "bf16", True, 3201)
+    per = w.M * w.D
+    assert w.H * per > 2**31
+    _say(f"{w} ({w.H * per} elements per tensor)")
+    dev = torch.device("cuda:0")
+    q, k, v = make_inputs_device(w, dev)
+    g = make_dout_device(w, dev)
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    s = scale_as_kernel(w.scale)
+    for h in sorted({0, 2**31 // per - 1, 2**31 // per, w.H - 1}):
+        q64, k64, v64, g64 = (x[0, h].double().cpu().numpy() for x in (q, k, v, g))
+        o_h = o[0, h].double().cpu().numpy()
+        rq, rk, rv, parts = oracle.head_bwd(q64, k64, v64, g64, s, w.causal, return_parts=True)
+        bq, bk, bv = bounds(parts, q64, k64, g64, o_h, s, w.dtype)
+        for name, got, ref, bnd in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
+            check(f"{w.name} head {h} {name}", w.dtype, got[0, h].double().cpu().numpy(), ref, bnd)
+    del q, k, v, g, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()

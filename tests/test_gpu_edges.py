@@ -230,3 +230,41 @@ def test_fast_and_general_paths_agree(dtype, D, causal):
     check(f"fast_{dtype}_D{D}_c{int(causal)}", dtype, o1.double().cpu().numpy(), l1.cpu().numpy(), O_ref, L_ref)
     check(f"general_{dtype}_D{D}_c{int(causal)}", dtype, o2.double().cpu().numpy(), l2.cpu().numpy(), O_ref, L_ref)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype,D,causal,BH", [
+    ("bf16", 128, False, 16385),  # pipelined 16-bit kernel, 8 waves
+    ("f16", 64, True, 32769),     # pipelined 16-bit kernel, 4 waves, causal
+    ("bf16", 100, False, 20972),  # general 16-bit kernel (D not a multiple of 32)
+    ("f32", 32, True, 65537),     # fp32 kernel
+])
+def test_tensors_beyond_2_31_elements(dtype, D, causal, BH):
+    """Q, K, V and O of more than 2^31 elements each (small per-head extents,
+    many heads): every row of the first head, of the heads on either side of
+    the 2^31-element and 2^32-byte offsets and of the last head, against the
+    oracle.  Inputs are drawn on the GPU (seeded) and the checked heads copied
+    to the host."""
+    torch = _t()
+    from workloads import make_inputs_device
+
+    M = N = 1024
+    per = M * D
+    assert BH * per > 2**31
+    w = Workload(f"big_{dtype}_d{D}", 1, BH, M, N, D, dtype, causal, 1 / math.sqrt(D), 1201)
+    _say(f"{w} ({BH * per} elements per tensor)")
+    dev = torch.device("cuda:0")
+    q, k, v = make_inputs_device(w, dev)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    elt = 4 if dtype == "f32" else 2
+    heads = {0, BH - 1}
+    for off in (2**31, 2**32 // elt):
+        heads |= {off // per - 1, off // per}
+    heads = sorted(h for h in heads if 0 <= h < BH)
+    for h in heads:
+        qh, kh, vh = q[0, h].cpu(), k[0, h].cpu(), v[0, h].cpu()
+        O_ref, L_ref = oracle.attention(qh, kh, vh, w.scale, causal)
+        check(f"{w.name}[head {h}]", dtype, o[0, h].double().cpu().numpy(),
+              lse[0, h].cpu().numpy(), O_ref, L_ref)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()

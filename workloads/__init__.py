@@ -25,7 +25,8 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "BENCH_WORKLOAD", "make_inputs", "sample_rows",
+__all__ = ["Workload", "WORKLOADS", "BENCH_WORKLOAD", "make_inputs", "make_inputs_device",
+           "make_dout_device", "sample_rows",
            "metric_flops", "visible_pairs", "exact_flops", "compulsory_bytes", "DTYPE_CODES",
            "ELT_BYTES"]
 
@@ -102,6 +103,39 @@ def make_inputs(w: Workload):
     k = torch.randn(w.shape_kv(), generator=g, dtype=torch.float32)
     v = torch.randn(w.shape_kv(), generator=g, dtype=torch.float32)
     return q.to(tdt), k.to(tdt), v.to(tdt)
+
+
+def make_inputs_device(w: Workload, device):
+    """Seeded Q, K, V generated directly on a GPU, for shapes too large to draw
+    on the host in seconds (tensors beyond 2^31 elements).  Same recipe as
+    :func:`make_inputs` (fp32 standard normals in the order Q, K, V, then a
+    round-to-nearest-even cast) but from a device ``torch.Generator`` seeded
+    ``w.seed``, so the values differ from :func:`make_inputs`'.  Callers copy the
+    heads they check to the host for the oracle."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    out = []
+    for shape in (w.shape_q(), w.shape_kv(), w.shape_kv()):
+        x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+        if w.q_mult != 1.0 and not out:
+            x.mul_(w.q_mult)
+        out.append(x.to(tdt))
+        del x
+    return tuple(out)
+
+
+def make_dout_device(w: Workload, device):
+    """Seeded incoming gradient drawn on a GPU (device generator seeded
+    ``w.seed + 500000``), the large-shape counterpart of :func:`make_dout`."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed + 500000)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    return torch.randn(w.shape_q(), generator=g, dtype=torch.float32, device=device).to(tdt)
 
 
 def make_dout(w: Workload):
