@@ -1,7 +1,6 @@
 """The C-ABI library without a GPU: it loads, exports every symbol the header
 declares, and rejects every bad argument on the host before any HIP call."""
 
-import ctypes
 import math
 import os
 import re

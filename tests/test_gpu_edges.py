@@ -13,8 +13,6 @@ from workloads import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TDT = None
-
 
 def _t():
     import torch
