@@ -146,6 +146,19 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
+def _check_given(t, name, shape, dtype, device):
+    """A caller-supplied output or workspace tensor must match what the kernels
+    write through its pointer: shape, dtype, device and a contiguous layout."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
         stream=None, general: bool = False, splits: int | None = None, workspace=None):
     """O, LSE = attention forward of q [B,H,M,D], k/v [B,H,N,D] (device tensors).
@@ -174,10 +187,17 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    for t in (k, v):
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_given(out, "out", (B, H, M, D), q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    else:
+        _check_given(lse, "lse", (B, H, M), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -186,6 +206,8 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
         need = max(fa_splitkv_workspace_bytes(B, H, M, D, splits), 0)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        elif workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
         st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), B, H, M, N, D, scale, 1 if causal else 0, code,
                             splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -233,13 +255,21 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    for t in (k, v, o, dout, lse):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _check_given(t, name, like.shape, like.dtype, like.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if delta is None:
         delta = torch.empty((2, B, H, M), dtype=torch.float32, device=q.device)
-    elif delta.dtype != torch.float32 or delta.numel() < 2 * B * H * M or not delta.is_contiguous():
-        raise ValueError("delta must be a contiguous fp32 workspace of at least 2*B*H*M elements")
+    elif (delta.dtype != torch.float32 or delta.numel() < 2 * B * H * M
+          or not delta.is_contiguous() or delta.device != q.device):
+        raise ValueError("delta must be a contiguous fp32 workspace on q's device "
+                         "of at least 2*B*H*M elements")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):

@@ -201,3 +201,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         fa.load()
     with pytest.raises(ImportError):
         fa.fa_fwd(P, P, P, P, P, 1, 1, 1, 1, 8, 1.0, 0, 0, None)
+
+
+def test_binding_checks_caller_supplied_buffers():
+    """Output and workspace tensors handed to the binding must match what the
+    kernels write through their pointers; anything else is refused before a
+    launch (shape, dtype, device, layout)."""
+    import torch
+
+    from io_aware_tiled_fa_amd import _check_given
+
+    dev = torch.device("cpu")
+    good = torch.empty(2, 3, 5, 8, dtype=torch.float16)
+    _check_given(good, "out", (2, 3, 5, 8), torch.float16, dev)
+    with pytest.raises(ValueError, match="shape"):
+        _check_given(good, "out", (2, 3, 5, 9), torch.float16, dev)
+    with pytest.raises(TypeError, match="float32"):
+        _check_given(good, "out", (2, 3, 5, 8), torch.float32, dev)
+    with pytest.raises(ValueError, match="on cuda"):
+        _check_given(good, "out", (2, 3, 5, 8), torch.float16, torch.device("cuda:0"))
+    with pytest.raises(ValueError, match="contiguous"):
+        _check_given(good.transpose(2, 3).contiguous().transpose(2, 3), "out", (2, 3, 5, 8),
+                     torch.float16, dev)

@@ -266,3 +266,89 @@ def test_tensors_beyond_2_31_elements(dtype, D, causal, BH):
               lse[0, h].cpu().numpy(), O_ref, L_ref)
     del q, k, v, o, lse
     torch.cuda.empty_cache()
+
+
+def test_caller_supplied_outputs():
+    """Preallocated out/lse (and dq/dk/dv) are written in place with the same
+    values as freshly allocated ones; mismatched ones are refused before any
+    launch."""
+    torch = _t()
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in _inputs(1, 2, 70, 90, 64, "bf16", 1301))
+    o_ref, l_ref = fa.fwd(q, k, v, causal=True)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 2, 70), float("nan"), device=dev)
+    o2, l2 = fa.fwd(q, k, v, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == out.data_ptr() and l2.data_ptr() == lse.data_ptr()
+    assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
+    with pytest.raises(ValueError, match="shape"):
+        fa.fwd(q, k, v, out=torch.empty(1, 2, 69, 64, dtype=q.dtype, device=dev))
+    with pytest.raises(TypeError):
+        fa.fwd(q, k, v, lse=torch.empty(1, 2, 70, dtype=torch.float16, device=dev))
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.fwd(q, k, v, out=torch.empty(1, 2, 64, 70, dtype=q.dtype, device=dev).transpose(2, 3))
+    g = torch.ones_like(q)
+    dq, dk, dv = fa.bwd(q, k, v, o_ref, l_ref, g, causal=True)
+    bufs = [torch.full_like(x, float("nan")) for x in (q, k, v)]
+    fa.bwd(q, k, v, o_ref, l_ref, g, causal=True, dq=bufs[0], dk=bufs[1], dv=bufs[2])
+    torch.cuda.synchronize()
+    for got, want in zip(bufs, (dq, dk, dv)):
+        assert torch.equal(got, want)
+    with pytest.raises(ValueError, match="shape"):
+        fa.bwd(q, k, v, o_ref, l_ref, g, dk=torch.empty_like(q))
+
+
+def test_graph_capture_and_replay():
+    """fa_fwd, fa_fwd_splitkv and fa_bwd captured once in a HIP graph (through
+    torch.cuda.graph, on preallocated buffers) and replayed on three fresh sets
+    of inputs copied into the captured tensors, with eager calls between the
+    replays: every replay is bit-identical to the eager result."""
+    torch = _t()
+    dev = torch.device("cuda:0")
+    B, H, M, N, D = 2, 3, 300, 500, 128
+    shape_q, shape_kv = (B, H, M, D), (B, H, N, D)
+    q = torch.empty(shape_q, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(shape_kv, dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    g = torch.empty_like(q)
+    out, out_s = torch.empty_like(q), torch.empty_like(q)
+    lse, lse_s = (torch.empty(B, H, M, dtype=torch.float32, device=dev) for _ in range(2))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(2, B, H, M, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_splitkv_workspace_bytes(B, H, M, D, 4), dtype=torch.uint8, device=dev)
+
+    def load(seed):
+        qc, kc, vc = _inputs(B, H, M, N, D, "bf16", seed)
+        gc = _inputs(B, H, M, M, D, "bf16", seed + 1)[0]
+        for dst, src in ((q, qc), (k, kc), (v, vc), (g, gc)):
+            dst.copy_(src.to(dev))
+
+    def work():
+        fa.fwd(q, k, v, causal=True, out=out, lse=lse)
+        fa.fwd(q, k, v, causal=True, out=out_s, lse=lse_s, splits=4, workspace=ws)
+        fa.bwd(q, k, v, out, lse, g, causal=True, dq=dq, dk=dk, dv=dv, delta=delta)
+
+    load(1400)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()  # warm-up outside the capture (first-call caches)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for seed in (1401, 1402, 1403):
+        _say(f"graph replay seed={seed}")
+        load(seed)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in (out, lse, out_s, lse_s, dq, dk, dv)]
+        o_e, l_e = fa.fwd(q, k, v, causal=True)
+        o_s, l_s = fa.fwd(q, k, v, causal=True, splits=4)
+        dq_e, dk_e, dv_e = fa.bwd(q, k, v, o_e, l_e, g, causal=True)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "lse", "out_split", "lse_split", "dq", "dk", "dv"), got,
+                              (o_e, l_e, o_s, l_s, dq_e, dk_e, dv_e)):
+            assert torch.equal(a, b), f"replay seed {seed}: {name} differs from eager"
