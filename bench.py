@@ -138,17 +138,19 @@ def f32_kernel(w):
         else "fa_fwd_f32_kernel"
 
 
-def load_traffic(w, kernel_ms):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match."""
+def load_traffic(w, key=None, source="fa_fwd.hip"):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match:
+    the record under ``key`` (default: the workload's name) in profiles/traffic.json,
+    taken while ``source`` had the digest stored with it."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE)).get(w.name)
+        rec = json.load(open(TRAFFIC_FILE)).get(key or w.name)
     except Exception:  # noqa: BLE001
         return None
     if not rec:
         return None
-    src = os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc", "fa_fwd.hip")
+    src = os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc", source)
     import hashlib
 
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -272,7 +274,7 @@ def main():
     tflops = fl_metric / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     achieved = fl_exact / (avg_launch_ms * 1e-3) / 1e12
-    traffic = None if args.splits else load_traffic(w, avg_launch_ms)
+    traffic = None if args.splits else load_traffic(w)
     log(f"ms/step {ms_per_step:.4f}  avg launch {avg_launch_ms:.4f} ms  median {med_launch_ms:.4f} ms  "
         f"{tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)  wall {wall:.3f}s")
 
@@ -448,7 +450,8 @@ def bench_bwd(args, w):
         },
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
+            "frac": round(achieved / peak, 4),
+            "traffic": load_traffic(w, key=w.name + "/bwd", source="fa_bwd.hip"),
             "kernel": "fa_bwd (delta + dkdv + dq kernels, one call)",
             "avg_launch_ms": round(avg_launch_ms, 5),
         },
