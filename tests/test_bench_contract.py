@@ -40,3 +40,27 @@ def test_bench_prints_one_contract_line():
     assert 0 < rl["frac"] < 1 and abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
+    """roofline.traffic comes from profiles/traffic.json only while the kernel
+    source still has the digest recorded with the counters; otherwise null."""
+    import hashlib
+
+    sys.path.insert(0, ROOT)
+    import bench
+    from workloads import WORKLOADS
+
+    w = WORKLOADS["causal_prefill_bf16"]
+    src = os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc", "fa_fwd.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({w.name: {"bytes_per_launch": 123, "source_sha256_16": digest},
+                             "other": {"bytes_per_launch": 7, "source_sha256_16": "0" * 16}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.load_traffic(w) == 123
+    assert bench.load_traffic(w, key="other") is None          # stale digest
+    assert bench.load_traffic(w, key="missing") is None
+    assert bench.load_traffic(w, source="fa_bwd.hip") is None  # digest of another file
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
+    assert bench.load_traffic(w) is None
