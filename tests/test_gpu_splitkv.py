@@ -48,6 +48,10 @@ CASES = [
     (_wl("split_bf16_empty_rows", 1, 2, 700, 300, 64, "bf16", True, 4104), 3),
     (_wl("split_f32_more_splits_than_tiles", 1, 1, 50, 100, 32, "f32", False, 4105), 64),
     (_wl("split_f16_d1", 1, 1, 33, 777, 1, "f16", True, 4106), 7),
+    # decode shape: one query row against 64K keys per head
+    (_wl("split_bf16_decode_64k", 2, 8, 1, 65536, 128, "bf16", False, 4107), 32),
+    # a short causal block at the end of a long context (bottom-right mask)
+    (_wl("split_f16_causal_tail_32k", 1, 4, 16, 32768, 64, "f16", True, 4108), 16),
 ]
 
 
