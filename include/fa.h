@@ -40,7 +40,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_PTR = 1,       /* a required pointer is NULL                               */
-  FA_ERR_BAD_SHAPE = 2,      /* B, H, M or N negative                                    */
+  FA_ERR_BAD_SHAPE = 2,      /* B, H, M or N negative, causal not 0/1, splits out of range */
   FA_ERR_BAD_DTYPE = 3,      /* dtype is not one of fa_dtype_t                            */
   FA_ERR_UNSUPPORTED_D = 4,  /* D outside 1..128                                          */
   FA_ERR_BAD_SCALE = 5,      /* scale not finite or not > 0                               */

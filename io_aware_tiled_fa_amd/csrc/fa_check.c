@@ -94,7 +94,8 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
-    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H, M, N must be >= 0 and causal 0 or 1";
+    case FA_ERR_BAD_SHAPE:
+      return "FA_ERR_BAD_SHAPE: B, H, M, N must be >= 0, causal 0 or 1, and splits 1..FA_MAX_SPLITS";
     case FA_ERR_BAD_DTYPE: return "FA_ERR_BAD_DTYPE: dtype must be F32, F16 or BF16";
     case FA_ERR_UNSUPPORTED_D: return "FA_ERR_UNSUPPORTED_D: head dim must be in 1..128";
     case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite and > 0";
