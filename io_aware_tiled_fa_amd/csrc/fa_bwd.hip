@@ -1179,7 +1179,9 @@ void launch_bwd_tiles(const BwdArgs& a) {
     if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
       if (a.M > 0) {
         const int items = (int)(a.BH * ktiles);
-        const int slots = persistent_workgroups(fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>, BT);
+        int slots = 0;  // the kernel loops over items at D >= 96 only
+        if constexpr (DP >= 96)
+          slots = persistent_workgroups<fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>>(BT);
         const int P = slots >= NXCD && slots < items ? slots : items;
         hipLaunchKernelGGL((fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>), dim3((unsigned)P),
                            dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k,
@@ -1200,7 +1202,9 @@ void launch_bwd_tiles(const BwdArgs& a) {
         constexpr int NW = DP == 64 ? 4 : 8;
         const int qtiles = (a.M + 32 * NW - 1) / (32 * NW);
         const int items = (int)(a.BH * qtiles);
-        const int slots = persistent_workgroups(fa_bwd_dq_fast_kernel<T, DP, NW>, 64 * NW);
+        int slots = 0;  // the kernel loops over items with 8 waves only
+        if constexpr (NW == 8)
+          slots = persistent_workgroups<fa_bwd_dq_fast_kernel<T, DP, NW>>(64 * NW);
         const int P = slots >= NXCD && slots < items ? slots : items;
         hipLaunchKernelGGL((fa_bwd_dq_fast_kernel<T, DP, NW>), dim3((unsigned)P), dim3(64 * NW), 0,
                            a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,

@@ -122,13 +122,16 @@ inline int device_cus() {
   return v;
 }
 
-// Workgroup count for a persistent launch of `kernel` (with `threads` threads)
+// Workgroup count for a persistent launch of KERNEL (with `threads` threads)
 // on the current device: one per CU when the occupancy calculator puts exactly
 // one workgroup on a CU, else 0 (launch one workgroup per item: co-resident
 // workgroups that start together stay in step and stop hiding each other's
-// prologue).  Cached per device; 0 too if the runtime cannot tell.
-template <class K>
-int persistent_workgroups(K kernel, int threads) {
+// prologue).  Cached per kernel and device (the kernel is a template argument,
+// so kernels that share a signature do not share the answer); 0 too if the
+// runtime cannot tell.  Only for kernels that loop over work items: a launch
+// of P < items workgroups leaves items undone in any other kernel.
+template <auto KERNEL>
+int persistent_workgroups(int threads) {
   static int cache[64];  // per device: -1 no, > 0 the count
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -136,7 +139,7 @@ int persistent_workgroups(K kernel, int threads) {
   if (v == 0) {
     int cus = 0, occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel),
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(KERNEL),
                                                      threads, 0) != hipSuccess)
       return 0;
     v = occ == 1 && cus > 0 ? cus : -1;

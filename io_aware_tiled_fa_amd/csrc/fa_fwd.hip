@@ -1123,7 +1123,10 @@ void launch_lp_fast_nw(const Launch& a) {
   const int items = (int)(a.BH * qtiles);
   // One workgroup per CU (persistent) where a workgroup fills a CU, else one
   // per item.  Every XCD range needs a workgroup of its own: at least NXCD.
-  const int slots = persistent_workgroups(fa_fwd_lp_pipe_kernel<T, DP, NW, elt>, 64 * NW);
+  // Only the 8-wave kernel loops over items; a 4-wave launch has one per item.
+  int slots = 0;
+  if constexpr (NW == 8)
+    slots = persistent_workgroups<fa_fwd_lp_pipe_kernel<T, DP, NW, elt>>(64 * NW);
   const int P = slots >= NXCD && slots < items ? slots : items;
   const KeySplit ks{a.N, 0, 0};
   hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, elt>), dim3((unsigned)P), dim3(64 * NW), 0,

@@ -352,3 +352,20 @@ def test_graph_capture_and_replay():
         for name, a, b in zip(("out", "lse", "out_split", "lse_split", "dq", "dk", "dv"), got,
                               (o_e, l_e, o_s, l_s, dq_e, dk_e, dv_e)):
             assert torch.equal(a, b), f"replay seed {seed}: {name} differs from eager"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_launch_history_does_not_change_results(dtype):
+    """A D = 64 forward and backward with more work items than compute units,
+    run in a fresh process right after a D = 128 one (whose kernels keep one
+    workgroup per CU): every output element is written and the last head, whose
+    items are scheduled last, matches the oracle (tests/persist_order_case.py)."""
+    import os
+    import subprocess
+    import sys
+
+    _say(f"launch history D=128 then D=64, {dtype}")
+    script = os.path.join(os.path.dirname(os.path.abspath(__file__)), "persist_order_case.py")
+    r = subprocess.run([sys.executable, script, dtype], capture_output=True, text=True, timeout=300)
+    print(r.stdout[-3000:], flush=True)
+    assert r.returncode == 0 and "ORDER_CASE_OK" in r.stdout, r.stderr[-3000:]
