@@ -12,6 +12,7 @@ import itertools
 import json
 import math
 import os
+import struct
 
 import numpy as np
 
@@ -29,6 +30,12 @@ def _golden(name):
 
 def _rng(seed):
     return np.random.default_rng(seed)
+
+
+def _f32(x: float) -> float:
+    """x rounded to IEEE binary32 (round to nearest even) through its byte
+    encoding, independently of the oracle's own rounding helper."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
 
 
 # ---------------------------------------------------------------- printed values
@@ -158,7 +165,7 @@ def pin_brute_force():
         v = rng.standard_normal((N, D + 1))  # value width differs from D on purpose
         s = 0.7
         O, L = attention(q, k, v, s, causal)
-        Ob, Lb = _brute(q.tolist(), k.tolist(), v.tolist(), oracle.scale_as_kernel(s), causal)
+        Ob, Lb = _brute(q.tolist(), k.tolist(), v.tolist(), _f32(s), causal)
         Ob, Lb = np.array(Ob), np.array(Lb)
         assert np.array_equal(np.isneginf(L), np.isneginf(Lb)), (M, N, D, causal)
         fin = np.isfinite(Lb)
@@ -183,7 +190,7 @@ def pin_torch_sdpa_fp64():
         v = rng.standard_normal((2, 3, N, D))
         s = 1.0 / math.sqrt(D)
         O, L = attention(q, k, v, s, causal)
-        s64 = oracle.scale_as_kernel(s)
+        s64 = _f32(s)
         mask = None
         if causal:
             mask = torch.from_numpy(np.arange(N)[None, :] <= np.arange(M)[:, None] + (N - M))
@@ -208,7 +215,82 @@ def pin_scipy_softmax_rows():
     assert np.abs(P - softmax(S, axis=-1)).max() <= 1e-14
     assert np.abs(P.sum(axis=-1) - 1.0).max() <= 1e-14
     assert np.abs(O - P @ v).max() <= 1e-14
-    assert np.abs(S - oracle.scale_as_kernel(0.5) * (q @ k.T)).max() <= 1e-13
+    assert np.abs(S - _f32(0.5) * (q @ k.T)).max() <= 1e-13
+
+
+# ---------------------------------------------------------------- the scale argument
+
+def pin_scale_rounded_to_fp32():
+    """The library receives the scale as an fp32 argument, so the oracle's scale
+    is that fp32 value.  Literal binary32 values (nearest-even rounding):
+    1/sqrt(128) -> 0.0883883461356163 (fp16 would give 0.08837890625),
+    1/sqrt(96) -> 0.10206207633018494, 0.3 -> 0.30000001192092896; 1/8 and 0 are
+    exact."""
+    cases = [(1 / math.sqrt(128), 0.0883883461356163), (1 / math.sqrt(96), 0.10206207633018494),
+             (0.3, 0.30000001192092896), (-0.3, -0.30000001192092896), (0.125, 0.125),
+             (0.0, 0.0)]
+    for x, want in cases:
+        assert oracle.scale_as_kernel(x) == want, (x, oracle.scale_as_kernel(x), want)
+        assert _f32(x) == want
+
+
+def pin_scores_use_fp32_scale():
+    """End to end: S built here with the scale rounded through its binary32
+    encoding (no oracle helper) matches attention's S and LSE to 1e-13, at
+    scales whose fp16, bf16 or unrounded values differ from the fp32 one by
+    1e-8 .. 1e-3 relative (each far above the tolerance at these logits)."""
+    rng = _rng(31)
+    q = rng.standard_normal((6, 128)) * 3
+    k = rng.standard_normal((9, 128))
+    v = rng.standard_normal((9, 4))
+    for x in (1 / math.sqrt(128), 1 / math.sqrt(96), 0.3, -0.3):
+        s32 = _f32(x)
+        O, L, S, P = attention(q, k, v, x, False, return_sp=True)
+        S_here = s32 * (q @ k.T)
+        assert np.abs(S - S_here).max() <= 1e-13, x
+        mx = S_here.max(axis=1)
+        L_here = mx + np.log(np.exp(S_here - mx[:, None]).sum(axis=1))
+        assert np.abs(L - L_here).max() <= 1e-13, x
+
+
+def pin_zero_scale_uniform():
+    """scale = 0: every visible score is 0, so P is uniform over the visible
+    keys, O is their mean and LSE = ln(#visible); empty rows stay O = 0,
+    LSE = -inf."""
+    rng = _rng(32)
+    M, N = 13, 8
+    q = rng.standard_normal((M, 5)) * 4
+    k = rng.standard_normal((N, 5)) * 4
+    v = rng.standard_normal((N, 3))
+    for causal in (False, True):
+        O, L = attention(q, k, v, 0.0, causal)
+        for i in range(M):
+            n = N if not causal else max(0, i + N - M + 1)
+            if n == 0:
+                assert np.all(O[i] == 0.0) and np.isneginf(L[i])
+                continue
+            assert abs(L[i] - math.log(n)) <= 1e-14
+            assert np.abs(O[i] - v[:n].mean(axis=0)).max() <= 1e-14
+
+
+def pin_negative_scale():
+    """A negative scale weights the keys by exp(-|s| q.k): brute force on tiny
+    shapes, and the exact identity attention(q, k, v, -s) = attention(-q, k, v, s)
+    (negation is exact in binary floating point)."""
+    rng = _rng(33)
+    for M, N, D, causal in [(5, 7, 3, False), (7, 5, 4, True), (6, 6, 2, True)]:
+        q = rng.standard_normal((M, D)) * 2
+        k = rng.standard_normal((N, D))
+        v = rng.standard_normal((N, 2))
+        O, L = attention(q, k, v, -0.7, causal)
+        Ob, Lb = _brute(q.tolist(), k.tolist(), v.tolist(), _f32(-0.7), causal)
+        Ob, Lb = np.array(Ob), np.array(Lb)
+        assert np.array_equal(np.isneginf(L), np.isneginf(Lb))
+        fin = np.isfinite(Lb)
+        assert np.abs(L[fin] - Lb[fin]).max(initial=0.0) <= 1e-12
+        assert np.abs(O - Ob).max() <= 1e-12
+        O2, L2 = attention(-q, k, v, 0.7, causal)
+        assert np.array_equal(O, O2) and np.array_equal(L, L2)
 
 
 # ---------------------------------------------------------------- closed forms
@@ -223,7 +305,7 @@ def pin_single_key():
         O, L = attention(q, k, v, 0.3, causal)
         vis_rows = np.arange(9) + (1 - 9) >= 0 if causal else np.ones(9, bool)
         assert np.abs(O[vis_rows] - v[0]).max() <= 1e-15
-        assert np.abs(L[vis_rows] - oracle.scale_as_kernel(0.3) * (q @ k[0])[vis_rows]).max() <= 1e-13
+        assert np.abs(L[vis_rows] - _f32(0.3) * (q @ k[0])[vis_rows]).max() <= 1e-13
         assert np.all(O[~vis_rows] == 0.0) and np.all(np.isneginf(L[~vis_rows]))
 
 
@@ -282,7 +364,7 @@ def pin_shift_feature():
     O, L = attention(q, k, v, s, True)
     O2, L2 = attention(np.hstack([q, np.ones((12, 1))]), np.hstack([k, np.full((19, 1), c)]), v, s, True)
     assert np.abs(O - O2).max() <= 1e-13
-    assert np.abs(L2 - L - oracle.scale_as_kernel(s) * c).max() <= 1e-12
+    assert np.abs(L2 - L - _f32(s) * c).max() <= 1e-12
 
 
 def pin_permutation_and_future():

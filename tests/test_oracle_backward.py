@@ -25,12 +25,12 @@ from oracle.definition import masked_softmax, scores, visible_mask
 SCALE = 0.5  # exact in fp32, so the oracle's fp32-rounded scale is this value
 
 
-def _loss(q, k, v, g, causal):
-    O, _ = oracle.attention(q, k, v, SCALE, causal)
+def _loss(q, k, v, g, causal, scale=SCALE):
+    O, _ = oracle.attention(q, k, v, scale, causal)
     return float(np.sum(O * g))
 
 
-def _fd_grads(q, k, v, g, causal, h=1e-6):
+def _fd_grads(q, k, v, g, causal, h=1e-6, scale=SCALE):
     """Central differences of sum(O * g) with respect to every input element."""
     grads = []
     for which in range(3):
@@ -43,7 +43,7 @@ def _fd_grads(q, k, v, g, causal, h=1e-6):
             xm = [x.copy() for x in xs]
             xp[which][idx] += h
             xm[which][idx] -= h
-            gx[idx] = (_loss(*xp, g, causal) - _loss(*xm, g, causal)) / (2 * h)
+            gx[idx] = (_loss(*xp, g, causal, scale) - _loss(*xm, g, causal, scale)) / (2 * h)
         grads.append(gx)
     return grads
 
@@ -75,6 +75,21 @@ def test_gradients_match_finite_differences(M, N, D, causal):
     fq, fk, fv = _fd_grads(q, k, v, g, causal)
     for a, b in ((dq, fq), (dk, fk), (dv, fv)):
         assert np.max(np.abs(a - b)) <= 1e-7 * max(1.0, np.max(np.abs(b)))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.75])
+@pytest.mark.parametrize("M,N,D,causal", [(3, 5, 2, False), (6, 3, 2, True)])
+def test_gradients_any_finite_scale(M, N, D, causal, scale):
+    """Zero and negative scales (exact in fp32): the gradients still match
+    central differences of the forward definition; at scale 0 dq and dk vanish
+    (the scores do not depend on q or k)."""
+    q, k, v, g = _inputs(M, N, D, 200 + M * 10 + N)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, g, scale, causal)
+    fq, fk, fv = _fd_grads(q, k, v, g, causal, scale=scale)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.max(np.abs(a - b)) <= 1e-7 * max(1.0, np.max(np.abs(b)))
+    if scale == 0.0:
+        assert np.all(dq == 0.0) and np.all(dk == 0.0)
 
 
 def _mutant(q, k, v, g, causal, defect):

@@ -6,7 +6,10 @@ import math
 import numpy as np
 import pytest
 
+import oracle
+import oracle.backward as ob
 import oracle.definition as oa
+import oracle.split as osp
 from oracle_pins import PINS
 
 _orig_scores = oa.scores
@@ -85,6 +88,37 @@ MUTANTS = {
     "empty_row_unguarded": ("masked_softmax", _softmax_empty_nan),
     "last_key_dropped": ("masked_softmax", _softmax_drop_last_key),
 }
+
+
+def _bf16(s):
+    import torch
+
+    return float(torch.tensor(s, dtype=torch.float64).to(torch.bfloat16).double())
+
+
+# Wrong roundings of the fp32 scale argument, planted in every module that
+# binds the helper (the definition, the split and backward oracles, the package).
+SCALE_MUTANTS = {
+    "scale_rounded_to_fp16": lambda s: float(np.float16(s)),
+    "scale_rounded_to_bf16": _bf16,
+    "scale_not_rounded": lambda s: float(s),
+    "scale_sign_dropped": lambda s: abs(float(np.float32(s))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCALE_MUTANTS))
+def test_scale_mutant_is_caught(name, monkeypatch):
+    fn = SCALE_MUTANTS[name]
+    for mod in (oa, ob, osp, oracle):
+        monkeypatch.setattr(mod, "scale_as_kernel", fn)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception:  # noqa: BLE001 - any failure of a pin counts as caught
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
