@@ -127,15 +127,102 @@ def cpu_baseline_bwd(w, qc, kc, vc, gc, budget_s: float = 15.0):
     }
 
 
-def f32_kernel(w):
-    """The fp32 kernel fa_fwd launches: the key-split one when D <= 64 and the
-    plain grid (128 query rows per workgroup) would fill under half the CUs."""
+def fwd_kernel_name(w, splits=0, cus=None):
+    """The forward kernel(s) one fa_fwd (splits = 0) or fa_fwd_splitkv call
+    launches for workload w, by the dispatch rules of fa_fwd.hip: fp16/bf16
+    with D in {64, 96, 128} run the pipelined direct-to-LDS kernel (split-KV
+    too), other 16-bit head dims the general kernel, fp32 the fp32 kernel (the
+    key-split one for small plain grids)."""
+    if w.dtype == "f32":
+        if splits:
+            name = "fa_fwd_f32_kernel"
+        else:
+            if cus is None:
+                import torch
+
+                cus = torch.cuda.get_device_properties(0).multi_processor_count
+            grid = w.B * w.H * ((w.M + 127) // 128)
+            name = ("fa_fwd_f32_ksplit_kernel" if w.D <= 64 and w.N > 0 and 2 * grid < cus
+                    else "fa_fwd_f32_kernel")
+    elif w.D in (64, 96, 128) and w.N > 0:
+        name = "fa_fwd_lp_pipe_kernel"
+    else:
+        name = "fa_fwd_lp_kernel"
+    return name + " + fa_merge_kernel (split-KV)" if splits and w.N > 0 else name
+
+
+class SclkSampler:
+    """Samples the GPU's current shader clock (MHz) from the driver's sysfs
+    table (the level marked '*' in pp_dpm_sclk) on a background thread while
+    the timed batches run; `summary()` gives the median and range, or None
+    where the file is not readable."""
+
+    def __init__(self, period_s: float = 0.01):
+        import glob
+        import threading
+
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        vals = []
+        for p in self.paths:
+            try:
+                for line in open(p):
+                    if line.rstrip().endswith("*"):
+                        vals.append(float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0]))
+            except (OSError, ValueError, IndexError):
+                continue
+        return max(vals) if vals else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"median_mhz": xs[len(xs) // 2], "min_mhz": xs[0], "max_mhz": xs[-1],
+                "samples": len(xs), "source": "sysfs pp_dpm_sclk (current level)"}
+
+
+def timed_batches(step, stream, est_ms: float, batches: int = 5, min_batch_ms: float = 100.0):
+    """The timing procedure for the reported distribution: `batches` batches of
+    R back-to-back launches each, R chosen so a batch lasts at least
+    min_batch_ms, each timed with HIP events on the launch stream.  Returns the
+    per-launch mean of every batch (ms), R, and the clock sampled meanwhile."""
     import torch
 
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    grid = w.B * w.H * ((w.M + 127) // 128)
-    return "fa_fwd_f32_ksplit_kernel" if w.D <= 64 and w.N > 0 and 2 * grid < cus \
-        else "fa_fwd_f32_kernel"
+    R = max(1, int(math.ceil(min_batch_ms / max(est_ms, 1e-6))))
+    per = []
+    with SclkSampler() as clk:
+        for _ in range(batches):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(R):
+                step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) / R)
+    return per, R, clk.summary()
 
 
 def load_traffic(w, key=None, source="fa_fwd.hip"):
@@ -167,6 +254,10 @@ def main():
     ap.add_argument("--workload", default=BENCH_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--batches", type=int, default=5,
+                    help="timed batches after the K steps (median and minimum are reported)")
+    ap.add_argument("--batch-ms", type=float, default=100.0,
+                    help="minimum duration of one timed batch (launches per batch follow)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default, the headline metric) or the backward pass")
     ap.add_argument("--splits", type=int, default=0,
@@ -272,11 +363,16 @@ def main():
     fl_metric = metric_flops(w.B, w.H, w.M, w.N, w.D, w.causal)
     fl_exact = exact_flops(w.B, w.H, w.M, w.N, w.D, w.causal)
     tflops = fl_metric / (ms_per_step * 1e-3) / 1e12
+    log(f"timed batches (>= 5 x >= {args.batch_ms:.0f} ms) ...")
+    per_batch, R, sclk = timed_batches(step, stream, avg_launch_ms, args.batches, args.batch_ms)
+    med_batch = sorted(per_batch)[len(per_batch) // 2]
     peak = PEAK_TFLOPS[w.dtype]
     achieved = fl_exact / (avg_launch_ms * 1e-3) / 1e12
     traffic = None if args.splits else load_traffic(w)
     log(f"ms/step {ms_per_step:.4f}  avg launch {avg_launch_ms:.4f} ms  median {med_launch_ms:.4f} ms  "
         f"{tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} peak)  wall {wall:.3f}s")
+    log(f"batches of {R}: median {med_batch:.4f} ms/launch ({fl_metric / (med_batch * 1e-3) / 1e12:.1f} "
+        f"TFLOP/s), min {min(per_batch):.4f} ms; sclk {sclk}")
 
     out = {
         "metric": METRIC,
@@ -304,14 +400,20 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": (("fa_fwd_f32_kernel" if w.dtype == "f32" else "fa_fwd_lp_kernel")
-                       + " + fa_merge_kernel (split-KV)" if args.splits else
-                       f32_kernel(w) if w.dtype == "f32" else
-                       "fa_fwd_lp_pipe_kernel" if w.D in (64, 96, 128) else "fa_fwd_lp_kernel"),
+            "kernel": fwd_kernel_name(w, args.splits),
             "avg_launch_ms": round(avg_launch_ms, 5),
             "median_launch_ms": round(med_launch_ms, 5),
             "min_launch_ms": round(min(launch_ms), 5),
             "hbm_gbs_compulsory": round(compulsory_bytes(w) / (avg_launch_ms * 1e-3) / 1e9, 1),
+        },
+        "timing": {
+            "procedure": f"{len(per_batch)} batches of {R} back-to-back launches after the K "
+                         "timed steps, HIP events on the launch stream, per-launch mean per batch",
+            "batches": len(per_batch), "launches_per_batch": R,
+            "batch_ms_per_launch": [round(x, 5) for x in per_batch],
+            "median_ms": round(med_batch, 5), "min_ms": round(min(per_batch), 5),
+            "median_tflops": round(fl_metric / (med_batch * 1e-3) / 1e12, 3),
+            "sclk": sclk,
         },
     }
     if not args.no_cpu_baseline:

@@ -43,7 +43,7 @@ typedef enum {
   FA_ERR_BAD_SHAPE = 2,      /* B, H, M or N negative, causal not 0/1, splits out of range */
   FA_ERR_BAD_DTYPE = 3,      /* dtype is not one of fa_dtype_t                            */
   FA_ERR_UNSUPPORTED_D = 4,  /* D outside 1..128                                          */
-  FA_ERR_BAD_SCALE = 5,      /* scale not finite or not > 0                               */
+  FA_ERR_BAD_SCALE = 5,      /* scale not finite, or scale*log2(e) overflows fp32         */
   FA_ERR_MISALIGNED = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte       */
   FA_ERR_TOO_LARGE = 7,      /* a per-head extent or the grid exceeds the 32-bit limits   */
   FA_ERR_HIP = 8,            /* the HIP runtime reported an error at launch               */
@@ -63,7 +63,10 @@ typedef enum {
  *   v    [B, H, N, D]  contiguous row-major, element type `dtype`
  *   o    [B, H, M, D]  contiguous row-major, element type `dtype` (written)
  *   lse  [B, H, M]     contiguous fp32, natural-log units (written)
- *   scale              the multiplier of Q K^T (typically 1/sqrt(D)); finite, > 0
+ *   scale              the multiplier of Q K^T (typically 1/sqrt(D)); any finite value
+ *                      with |scale * log2(e)| finite in fp32 (|scale| < 2.36e38):
+ *                      negative scales weight small scores up, and scale 0 gives
+ *                      uniform weights over the visible keys (LSE = ln #visible)
  *   causal             0: every key visible; 1: bottom-right causal mask
  *   dtype              an fa_dtype_t value
  *   stream             a hipStream_t, or NULL for the default stream
@@ -138,7 +141,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 /*
  * fa_splitkv_workspace_bytes - bytes of workspace fa_fwd_splitkv needs for
  * these sizes: splits * B * H * M * (D + 1) * 4.  Returns -1 for negative
- * sizes, D < 1 or splits < 1.
+ * sizes, D outside 1..128, splits < 1, or a size beyond int64.
  */
 int64_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D, int splits);
 
@@ -171,9 +174,9 @@ int fa_splitkv_check_args(const void* q, const void* k, const void* v, const voi
  *   dout [B, H, M, D]  element type `dtype`: dLoss/dO (read)
  *   dq   [B, H, M, D], dk [B, H, N, D], dv [B, H, N, D]  element type `dtype` (written)
  *   delta [2, B, H, M] fp32 workspace (written; on return delta[0] holds
- *                      -Delta_i and delta[1] holds -LSE_i / scale, 0 where
- *                      LSE_i = -inf: per-row terms the kernels fold into
- *                      their accumulators)
+ *                      -Delta_i and delta[1] holds -LSE_i / |scale| (-LSE_i
+ *                      for scale 0), 0 where LSE_i = -inf: per-row terms the
+ *                      kernels fold into their accumulators)
  *   scale, causal, stream  as for fa_fwd
  *   dtype        FA_DTYPE_F16 or FA_DTYPE_BF16 (FA_DTYPE_F32 returns
  *                FA_ERR_BAD_DTYPE in this version)
@@ -205,8 +208,9 @@ int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o
 /* fa_status_string - a static, human-readable name for a status code. */
 const char* fa_status_string(int status);
 
-/* fa_abi_version - the ABI revision of this header (currently 4: 3 added fa_bwd
- * and fa_fwd_splitkv; 4 doubled fa_bwd's workspace to [2, B, H, M]). */
+/* fa_abi_version - the ABI revision of this header (currently 5: 3 added fa_bwd
+ * and fa_fwd_splitkv; 4 doubled fa_bwd's workspace to [2, B, H, M]; 5 accepts
+ * zero and negative scales). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

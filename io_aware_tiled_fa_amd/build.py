@@ -13,6 +13,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -54,9 +55,12 @@ def build(verbose: bool = False) -> str:
     check_o = os.path.join(BUILD, "fa_check.o")
     fwd_o = os.path.join(BUILD, "fa_fwd.o")
     bwd_o = os.path.join(BUILD, "fa_bwd.o")
-    _run([cc, *C_FLAGS, "-c", os.path.join(CSRC, "fa_check.c"), "-o", check_o], verbose)
-    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_fwd.hip"), "-o", fwd_o], verbose)
-    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_bwd.hip"), "-o", bwd_o], verbose)
+    steps = [[cc, *C_FLAGS, "-c", os.path.join(CSRC, "fa_check.c"), "-o", check_o],
+             [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_fwd.hip"), "-o", fwd_o],
+             [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_bwd.hip"), "-o", bwd_o]]
+    with ThreadPoolExecutor(max_workers=len(steps)) as pool:  # independent translation units
+        for f in [pool.submit(_run, cmd, verbose) for cmd in steps]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, fwd_o, bwd_o, check_o],
          verbose)

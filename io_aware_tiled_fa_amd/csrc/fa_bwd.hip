@@ -59,7 +59,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Per query row, into the two halves of the workspace:
 //   ws[row]        = -Delta_i, Delta_i = sum_d dO[i, d] * O[i, d] in fp32;
-//   ws[rows + row] = -L_i / scale (0 where L_i = -inf: the row sees no key).
+//   ws[rows + row] = -L_i / s (0 where L_i = -inf: the row sees no key), s the
+//   positive scale of the score product (|scale|, or 1 for scale 0: fold_scale).
 // The fast dK/dV kernel loads them as the initial values of the dP and S
 // accumulators, so that the MFMAs leave dP - Delta and S - L / scale, and
 // P = exp2(c * acc) with c = scale * log2(e).  16 lanes per row.
@@ -215,7 +216,8 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dk,
-    typename T::elt* __restrict__ dv, int M, int N, int D, int ktiles, float c, float scale) {
+    typename T::elt* __restrict__ dv, int M, int N, int D, int ktiles, float c, float scale,
+    QFold qf) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using St = Stager<T, DP, BQ, DFULL>;
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_kernel(
   vec8 kb[KK], vb[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    kb[kk] = load_row8<T, DFULL>(Kh, key, N, D, 16 * kk + 8 * h);
+    kb[kk] = fold_vec(load_row8<T, DFULL>(Kh, key, N, D, 16 * kk + 8 * h), qf);
     vb[kk] = load_row8<T, DFULL>(Vh, key, N, D, 16 * kk + 8 * h);
   }
   f32x16 dka[DT], dva[DT];
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dk,
     typename T::elt* __restrict__ dv, int M, int N, int ktiles, int items, float c, float scale,
-    int causal) {
+    int causal, QFold qf) {
   // lse is unused here: `delta` points at the workspace [2, B*H*M], whose
   // second half holds -L / scale per row (see fa_bwd_delta_kernel).
   using elt = typename T::elt;
@@ -762,7 +764,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     if (qt0 + i < nqt) issue(qt0 + i);
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    kb[kk] = load_row8<T, true>(Kh, key, N, D, 16 * kk + 8 * h);
+    kb[kk] = fold_vec(load_row8<T, true>(Kh, key, N, D, 16 * kk + 8 * h), qf);
     vb[kk] = load_row8<T, true>(Vh, key, N, D, 16 * kk + 8 * h);
   }
   if (qt0 < nqt) {
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dq,
-    int M, int N, int D, int qtiles, float c, float scale) {
+    int M, int N, int D, int qtiles, float c, float scale, QFold qf) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using St = Stager<T, DP, BNK, DFULL>;
@@ -864,7 +866,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
   vec8 qb[KK], gb[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    qb[kk] = load_row8<T, DFULL>(Qh, qrow, M, D, 16 * kk + 8 * h);
+    qb[kk] = fold_vec(load_row8<T, DFULL>(Qh, qrow, M, D, 16 * kk + 8 * h), qf);
     gb[kk] = load_row8<T, DFULL>(Gh, qrow, M, D, 16 * kk + 8 * h);
   }
   float l2 = 0.0f, dl = 0.0f;
@@ -964,7 +966,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dq,
-    int M, int N, int qtiles, int items, float c, float scale, int causal) {
+    int M, int N, int qtiles, int items, float c, float scale, int causal, QFold qf) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using L = FastLayout<DP>;
@@ -1018,7 +1020,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
   vec8 qb[KK], gb[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    qb[kk] = load_row8<T, true>(Qh, qrow, M, D, 16 * kk + 8 * h);
+    qb[kk] = fold_vec(load_row8<T, true>(Qh, qrow, M, D, 16 * kk + 8 * h), qf);
     gb[kk] = load_row8<T, true>(Gh, qrow, M, D, 16 * kk + 8 * h);
   }
   float l2 = 0.0f, dl = 0.0f;
@@ -1157,7 +1159,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Host dispatch.
+// Host dispatch.  Every launch returns its own status (see `launch`).
 
 struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
@@ -1166,13 +1168,18 @@ struct BwdArgs {
   float* delta;
   int64_t BH;
   int M, N, D;
-  float c, scale;
+  float c;      // positive exponent constant of the score product (fold_scale)
+  float s_eff;  // positive scale of the score product (the row statistics use it)
+  float scale;  // the caller's scale: the factor of dQ and dK
+  QFold qf;     // sign fold of the stationary score operand (K in dK/dV, Q in dQ)
   hipStream_t stream;
+  int dev;      // device of `stream`
 };
 
 template <class T, int DP, bool CAUSAL, bool DFULL>
-void launch_bwd_tiles(const BwdArgs& a) {
+hipError_t launch_bwd_tiles(const BwdArgs& a) {
   using elt = typename T::elt;
+  hipError_t e = hipSuccess;
   if (a.N > 0) {
     const int ktiles = (a.N + BK - 1) / BK;
     bool done = false;
@@ -1181,20 +1188,21 @@ void launch_bwd_tiles(const BwdArgs& a) {
         const int items = (int)(a.BH * ktiles);
         int slots = 0;  // the kernel loops over items at D >= 96 only
         if constexpr (DP >= 96)
-          slots = persistent_workgroups<fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>>(BT);
+          slots = persistent_workgroups<fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>>(BT, a.dev);
         const int P = slots >= NXCD && slots < items ? slots : items;
-        hipLaunchKernelGGL((fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>), dim3((unsigned)P),
-                           dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k,
-                           (const elt*)a.v, (const elt*)a.dout, a.lse, a.delta, (elt*)a.dk,
-                           (elt*)a.dv, a.M, a.N, ktiles, items, a.c, a.scale, CAUSAL ? 1 : 0);
+        e = launch(fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>, dim3((unsigned)P), dim3(BT),
+                   a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
+                   (const elt*)a.dout, a.lse, (const float*)a.delta, (elt*)a.dk, (elt*)a.dv, a.M,
+                   a.N, ktiles, items, a.c, a.scale, CAUSAL ? 1 : 0, a.qf);
         done = true;
       }
     }
     if (!done)
-      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, DP, CAUSAL, DFULL>), dim3((unsigned)(a.BH * ktiles)),
-                         dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
-                         (const elt*)a.dout, a.lse, a.delta, (elt*)a.dk, (elt*)a.dv, a.M, a.N, a.D,
-                         ktiles, a.c, a.scale);
+      e = launch(fa_bwd_dkdv_kernel<T, DP, CAUSAL, DFULL>, dim3((unsigned)(a.BH * ktiles)),
+                 dim3(BT), a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
+                 (const elt*)a.dout, a.lse, (const float*)a.delta, (elt*)a.dk, (elt*)a.dv, a.M,
+                 a.N, a.D, ktiles, a.c, a.scale, a.qf);
+    if (e != hipSuccess) return e;
   }
   if (a.M > 0) {
     if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
@@ -1204,42 +1212,44 @@ void launch_bwd_tiles(const BwdArgs& a) {
         const int items = (int)(a.BH * qtiles);
         int slots = 0;  // the kernel loops over items with 8 waves only
         if constexpr (NW == 8)
-          slots = persistent_workgroups<fa_bwd_dq_fast_kernel<T, DP, NW>>(64 * NW);
+          slots = persistent_workgroups<fa_bwd_dq_fast_kernel<T, DP, NW>>(64 * NW, a.dev);
         const int P = slots >= NXCD && slots < items ? slots : items;
-        hipLaunchKernelGGL((fa_bwd_dq_fast_kernel<T, DP, NW>), dim3((unsigned)P), dim3(64 * NW), 0,
-                           a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
-                           (const elt*)a.dout, a.lse, a.delta, (elt*)a.dq, a.M, a.N, qtiles, items,
-                           a.c, a.scale, CAUSAL ? 1 : 0);
-        return;
+        return launch(fa_bwd_dq_fast_kernel<T, DP, NW>, dim3((unsigned)P), dim3(64 * NW),
+                      a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
+                      (const elt*)a.dout, a.lse, (const float*)a.delta, (elt*)a.dq, a.M, a.N,
+                      qtiles, items, a.c, a.scale, CAUSAL ? 1 : 0, a.qf);
       }
     }
     const int qtiles = (a.M + BMQ - 1) / BMQ;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, DP, CAUSAL, DFULL>), dim3((unsigned)(a.BH * qtiles)),
-                       dim3(BT), 0, a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
-                       (const elt*)a.dout, a.lse, a.delta, (elt*)a.dq, a.M, a.N, a.D, qtiles, a.c,
-                       a.scale);
+    return launch(fa_bwd_dq_kernel<T, DP, CAUSAL, DFULL>, dim3((unsigned)(a.BH * qtiles)),
+                  dim3(BT), a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
+                  (const elt*)a.dout, a.lse, (const float*)a.delta, (elt*)a.dq, a.M, a.N, a.D,
+                  qtiles, a.c, a.scale, a.qf);
   }
+  return e;
 }
 
 template <class T, int DP, bool CAUSAL>
-void dispatch_full(const BwdArgs& a) {
-  if (a.D == DP) launch_bwd_tiles<T, DP, CAUSAL, true>(a);
-  else launch_bwd_tiles<T, DP, CAUSAL, false>(a);
+hipError_t dispatch_full(const BwdArgs& a) {
+  if (a.D == DP) return launch_bwd_tiles<T, DP, CAUSAL, true>(a);
+  return launch_bwd_tiles<T, DP, CAUSAL, false>(a);
 }
 
 template <class T, bool CAUSAL>
-void dispatch_bwd(const BwdArgs& a) {
+hipError_t dispatch_bwd(const BwdArgs& a) {
   if (a.M > 0) {
     const int64_t rows = a.BH * a.M;
     const int64_t blocks = (rows + 15) / 16;
-    hipLaunchKernelGGL((fa_bwd_delta_kernel<T>), dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
-                       dim3(BT), 0, a.stream, (const typename T::elt*)a.o,
-                       (const typename T::elt*)a.dout, a.lse, a.delta, rows, a.D, a.scale);
+    const hipError_t e = launch(fa_bwd_delta_kernel<T>, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                                dim3(BT), a.stream, (const typename T::elt*)a.o,
+                                (const typename T::elt*)a.dout, a.lse, a.delta, rows, a.D,
+                                a.s_eff);
+    if (e != hipSuccess) return e;
   }
-  if (a.D <= 32) dispatch_full<T, 32, CAUSAL>(a);
-  else if (a.D <= 64) dispatch_full<T, 64, CAUSAL>(a);
-  else if (a.D <= 96) dispatch_full<T, 96, CAUSAL>(a);
-  else dispatch_full<T, 128, CAUSAL>(a);
+  if (a.D <= 32) return dispatch_full<T, 32, CAUSAL>(a);
+  if (a.D <= 64) return dispatch_full<T, 64, CAUSAL>(a);
+  if (a.D <= 96) return dispatch_full<T, 96, CAUSAL>(a);
+  return dispatch_full<T, 128, CAUSAL>(a);
 }
 
 }  // namespace
@@ -1267,12 +1277,17 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.M = (int)M;
   a.N = (int)N;
   a.D = (int)D;
-  // The same fp32 constant as the forward pass: exp2(s * c - L * log2 e).
-  a.c = (float)((double)scale * 1.4426950408889634074);
+  // The same fp32 constant as the forward pass: exp2(s * c - L * log2 e), with
+  // the scale's sign moved into the stationary score operand.
+  const ScaleFold f = fold_scale(scale, 2);
+  a.c = f.c;
+  a.s_eff = f.s_eff;
   a.scale = scale;
+  a.qf = f.q;
   a.stream = (hipStream_t)stream;
-  (void)hipGetLastError();
-  if (dtype == FA_DTYPE_F16) causal ? dispatch_bwd<TF16, true>(a) : dispatch_bwd<TF16, false>(a);
-  else causal ? dispatch_bwd<TBF16, true>(a) : dispatch_bwd<TBF16, false>(a);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+  a.dev = stream_device(a.stream);
+  const hipError_t e = dtype == FA_DTYPE_F16
+                           ? (causal ? dispatch_bwd<TF16, true>(a) : dispatch_bwd<TF16, false>(a))
+                           : (causal ? dispatch_bwd<TBF16, true>(a) : dispatch_bwd<TBF16, false>(a));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

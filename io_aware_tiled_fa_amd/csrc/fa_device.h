@@ -109,11 +109,19 @@ __device__ __forceinline__ TileCoord item_coord(int t, int qtiles) {
   return c;
 }
 
-// Compute units of the current device (cached per device; 0 if unknown).
-inline int device_cus() {
-  static int cache[64];
+// Device a stream belongs to (the current device for the null stream, or if
+// the runtime cannot tell).
+inline int stream_device(hipStream_t stream) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) == hipSuccess) return dev;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  return dev;
+}
+
+// Compute units of device `dev` (cached per device; 0 if unknown).
+inline int device_cus(int dev) {
+  static int cache[64];
+  if (dev < 0 || dev >= 64) return 0;
   int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
   if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
@@ -123,18 +131,19 @@ inline int device_cus() {
 }
 
 // Workgroup count for a persistent launch of KERNEL (with `threads` threads)
-// on the current device: one per CU when the occupancy calculator puts exactly
-// one workgroup on a CU, else 0 (launch one workgroup per item: co-resident
+// on device `dev`: one per CU when the occupancy calculator puts exactly one
+// workgroup on a CU, else 0 (launch one workgroup per item: co-resident
 // workgroups that start together stay in step and stop hiding each other's
 // prologue).  Cached per kernel and device (the kernel is a template argument,
 // so kernels that share a signature do not share the answer); 0 too if the
 // runtime cannot tell.  Only for kernels that loop over work items: a launch
-// of P < items workgroups leaves items undone in any other kernel.
+// of P < items workgroups leaves items undone in any other kernel.  (The
+// occupancy depends only on the kernel's resources and the architecture, the
+// same on every gfx950 device.)
 template <auto KERNEL>
-int persistent_workgroups(int threads) {
+int persistent_workgroups(int threads, int dev) {
   static int cache[64];  // per device: -1 no, > 0 the count
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (dev < 0 || dev >= 64) return 0;
   int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
   if (v == 0) {
     int cus = 0, occ = 0;
@@ -146,6 +155,20 @@ int persistent_workgroups(int threads) {
     __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
   }
   return v > 0 ? v : 0;
+}
+
+// Launch of a kernel that reports its own status: hipLaunchKernel's return
+// value, so no hipGetLastError call reads (and clears) an error the caller
+// has not looked at yet.
+template <class X>
+struct same_type {
+  using type = X;
+};
+template <class... P>
+hipError_t launch(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                  typename same_type<P>::type... args) {
+  void* argv[] = {(void*)&args..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, 0, stream);
 }
 
 // Lanes l and l^32 hold the same query row (different keys).  v_permlane32_swap
@@ -194,6 +217,45 @@ struct FastLayout {
   }
 };
 
+
+// Sign of the scale.  Every kernel takes the row maximum of raw scores q.k and
+// multiplies it by c = scale*log2(e) afterwards, and masks invisible keys with
+// -inf before that multiply; both need c > 0.  For c < 0, S*c equals
+// ((-Q) K^T)*|c| exactly (negation is exact and the MFMA's round-to-nearest is
+// symmetric under it), and for c == 0 every score is 0 = (0*Q) K^T.  So the
+// operand that enters the score product from registers (Q in the forward and
+// dQ kernels, K in the dK/dV kernels) is sign-flipped or zeroed as it is
+// loaded, word by word as (x & qand) ^ qxor, and the kernels see a positive c.
+struct QFold {
+  unsigned qand;
+  unsigned qxor;
+};
+__device__ __forceinline__ u32x4 fold_bits(u32x4 x, QFold f) { return (x & f.qand) ^ f.qxor; }
+template <class V>
+__device__ __forceinline__ V fold_vec(V x, QFold f) {
+  return __builtin_bit_cast(V, fold_bits(__builtin_bit_cast(u32x4, x), f));
+}
+__device__ __forceinline__ float fold_f32(float x, QFold f) {
+  return __uint_as_float((__float_as_uint(x) & f.qand) ^ f.qxor);
+}
+
+// Host side: the positive exponent constant c, the positive scale s_eff the
+// kernels' row statistics use (|scale|, or 1 for a zero scale, where every
+// score is 0 and any positive constant gives the uniform weights), and the fold
+// of the score operand.  `elt_bytes` is the element size of that operand.
+struct ScaleFold {
+  float c;
+  float s_eff;
+  QFold q;
+};
+inline ScaleFold fold_scale(float scale, int elt_bytes) {
+  const double log2e = 1.4426950408889634074;
+  const float c = (float)((double)scale * log2e);  // rounded once, as every exponential uses it
+  const unsigned sign = elt_bytes == 4 ? 0x80000000u : 0x80008000u;
+  if (c > 0.0f) return ScaleFold{c, scale, QFold{~0u, 0u}};
+  if (c < 0.0f) return ScaleFold{-c, -scale, QFold{~0u, sign}};
+  return ScaleFold{(float)log2e, 1.0f, QFold{0u, 0u}};
+}
 
 // Pins a value at this point of the instruction stream: an empty statement
 // that reads and rewrites it, so the arithmetic producing it cannot be moved

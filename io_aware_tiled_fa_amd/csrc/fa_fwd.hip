@@ -175,7 +175,7 @@ template <class T, int DP, bool CAUSAL, bool DFULL, class OUT>
 __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, OUT* __restrict__ o, float* __restrict__ lse, int M,
-    int Ntot, int D, int qtiles, float c, KeySplit ks) {
+    int Ntot, int D, int qtiles, float c, KeySplit ks, QFold qf) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   constexpr int KSTR = DP + 8;          // LDS row stride of K (elements)
@@ -228,13 +228,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
     if (DFULL) {
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (qrow < M) raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + d0);
-      qreg[kk] = __builtin_bit_cast(vec8, raw);
+      qreg[kk] = __builtin_bit_cast(vec8, fold_bits(raw, qf));
     } else {
       vec8 x;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         x[e] = (qrow < M && d0 + e < D) ? Qh[(int64_t)qrow * D + d0 + e] : (elt)0.0f;
-      qreg[kk] = x;
+      qreg[kk] = fold_vec(x, qf);
     }
   }
 
@@ -404,7 +404,7 @@ template <class T, int DP, int NW, class OUT>
 __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, OUT* __restrict__ o, float* __restrict__ lse, int M,
-    int Ntot, int off_all, int qtiles, int items, float c, KeySplit ks) {
+    int Ntot, int off_all, int qtiles, int items, float c, KeySplit ks, QFold qf) {
   constexpr bool CAUSAL = true;  // masking logic always on; `off` decides what it masks
   constexpr int D = DP;          // the dispatcher routes only D == DP here
   using elt = typename T::elt;
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   for (int kk = 0; kk < KK; ++kk) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (qrow < M) raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * kk + 8 * h);
-    qreg[kk] = __builtin_bit_cast(vec8, raw);
+    qreg[kk] = __builtin_bit_cast(vec8, fold_bits(raw, qf));
   }
 
   const int cp_sub = lane / L::SLOTS;
@@ -649,7 +649,7 @@ template <int DP, bool CAUSAL, bool DFULL>
 __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int M, int Ntot, int D, int qtiles, float c,
-    KeySplit ks) {
+    KeySplit ks, QFold qf) {
   constexpr int KSTR = DP + 1;
   constexpr int VSTR = DP + 4;
   constexpr int K_ELEMS = BN32 * KSTR;
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int d = 2 * s + h;
-    qreg[s] = (qrow < M && d < D) ? Qh[(int64_t)qrow * D + d] : 0.0f;
+    qreg[s] = fold_f32((qrow < M && d < D) ? Qh[(int64_t)qrow * D + d] : 0.0f, qf);
   }
 
   f32x16 acc[DT];
@@ -827,7 +827,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_f32_kernel(
 template <int DP, bool CAUSAL, bool DFULL>
 __global__ __launch_bounds__(NTHREADS, 1) void fa_fwd_f32_ksplit_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int M, int N, int D, int qtiles, float c) {
+    float* __restrict__ o, float* __restrict__ lse, int M, int N, int D, int qtiles, float c,
+    QFold qf) {
   constexpr int ROWS = 32;
   constexpr int KEYS = 4 * BN32;                // keys per step (all four waves)
   constexpr int KSTR = DP + 1;
@@ -869,7 +870,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fa_fwd_f32_ksplit_kernel(
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     const int d = 2 * st + h;
-    qreg[st] = (qrow < M && d < D) ? Qh[(int64_t)qrow * D + d] : 0.0f;
+    qreg[st] = fold_f32((qrow < M && d < D) ? Qh[(int64_t)qrow * D + d] : 0.0f, qf);
   }
 
   f32x16 acc[DT];
@@ -1065,7 +1066,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Host dispatch.
+// Host dispatch.  Every launch returns its own status (see `launch`).
 
 struct Launch {
   const void* q;
@@ -1074,38 +1075,38 @@ struct Launch {
   void* o;
   float* lse;
   int M, N, D, qtiles;
-  float c;
+  float c;    // positive exponent constant (see fold_scale)
+  QFold qf;   // sign fold of the Q operand
   dim3 grid;
   int64_t BH;
   hipStream_t stream;
+  int dev;       // device of `stream`
   bool generic;  // force the general kernel (register-staged tiles)
 };
 
 template <class T, int DP, bool CAUSAL>
-void launch_lp(const Launch& a) {
+hipError_t launch_lp(const Launch& a) {
   using elt = typename T::elt;
   const KeySplit ks{a.N, 0, 0};
   if (a.D == DP)
-    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, true, elt>), a.grid, dim3(NTHREADS), 0,
-                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
-                       a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
-  else
-    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, false, elt>), a.grid, dim3(NTHREADS), 0,
-                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
-                       a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
+    return launch(fa_fwd_lp_kernel<T, DP, CAUSAL, true, elt>, a.grid, dim3(NTHREADS), a.stream,
+                  (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N,
+                  a.D, a.qtiles, a.c, ks, a.qf);
+  return launch(fa_fwd_lp_kernel<T, DP, CAUSAL, false, elt>, a.grid, dim3(NTHREADS), a.stream,
+                (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N, a.D,
+                a.qtiles, a.c, ks, a.qf);
 }
 
 template <int DP, bool CAUSAL>
-void launch_f32(const Launch& a) {
+hipError_t launch_f32(const Launch& a) {
   const KeySplit ks{a.N, 0, 0};
   if (a.D == DP)
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, true>), a.grid, dim3(NTHREADS), 0,
-                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
-  else
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, false>), a.grid, dim3(NTHREADS), 0,
-                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (float*)a.o, a.lse, a.M, a.N, a.D, a.qtiles, a.c, ks);
+    return launch(fa_fwd_f32_kernel<DP, CAUSAL, true>, a.grid, dim3(NTHREADS), a.stream,
+                  (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.M,
+                  a.N, a.D, a.qtiles, a.c, ks, a.qf);
+  return launch(fa_fwd_f32_kernel<DP, CAUSAL, false>, a.grid, dim3(NTHREADS), a.stream,
+                (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.M,
+                a.N, a.D, a.qtiles, a.c, ks, a.qf);
 }
 
 // Waves per workgroup of the fast path (32 query rows each).  At D = 96 and 128
@@ -1115,7 +1116,7 @@ template <int DP>
 constexpr int fast_waves() { return DP == 64 ? 4 : 8; }
 
 template <class T, int DP, bool CAUSAL, int NW>
-void launch_lp_fast_nw(const Launch& a) {
+hipError_t launch_lp_fast_nw(const Launch& a) {
   using elt = typename T::elt;
   const int off = CAUSAL ? a.N - a.M : a.N;
   const int rows = 32 * NW;
@@ -1126,33 +1127,33 @@ void launch_lp_fast_nw(const Launch& a) {
   // Only the 8-wave kernel loops over items; a 4-wave launch has one per item.
   int slots = 0;
   if constexpr (NW == 8)
-    slots = persistent_workgroups<fa_fwd_lp_pipe_kernel<T, DP, NW, elt>>(64 * NW);
+    slots = persistent_workgroups<fa_fwd_lp_pipe_kernel<T, DP, NW, elt>>(64 * NW, a.dev);
   const int P = slots >= NXCD && slots < items ? slots : items;
   const KeySplit ks{a.N, 0, 0};
-  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, elt>), dim3((unsigned)P), dim3(64 * NW), 0,
-                     a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o,
-                     a.lse, a.M, a.N, off, qtiles, items, a.c, ks);
+  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, elt>, dim3((unsigned)P), dim3(64 * NW), a.stream,
+                (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N, off,
+                qtiles, items, a.c, ks, a.qf);
 }
 
 // At D = 96 and 128, when even 128-row workgroups (twice as many) leave a CU
 // for each, the grid runs on those: the same work on twice the CUs.  (Where
 // the doubled grid would put two workgroups on some CUs it measured slower.)
 template <class T, int DP, bool CAUSAL>
-void launch_lp_fast(const Launch& a) {
+hipError_t launch_lp_fast(const Launch& a) {
   constexpr int NW = fast_waves<DP>();
   if constexpr (NW == 8) {
     const int64_t wide = a.BH * ((a.M + 32 * NW - 1) / (32 * NW));
-    const int cus = device_cus();
+    const int cus = device_cus(a.dev);
     if (cus > 0 && a.BH * ((a.M + 127) / 128) <= cus && wide < cus)
       return launch_lp_fast_nw<T, DP, CAUSAL, 4>(a);
   }
-  launch_lp_fast_nw<T, DP, CAUSAL, NW>(a);
+  return launch_lp_fast_nw<T, DP, CAUSAL, NW>(a);
 }
 
 // Split-KV partials on the fast path (fp32 outputs into the workspace).
 template <class T, int DP, bool CAUSAL>
-void launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, float* opart,
-                          float* lpart) {
+hipError_t launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, float* opart,
+                                float* lpart) {
   using elt = typename T::elt;
   constexpr int NW = fast_waves<DP>();
   const int off = CAUSAL ? a.N - a.M : a.N;
@@ -1160,105 +1161,100 @@ void launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, float* opa
   const int qtiles = (a.M + rows - 1) / rows;
   const int items = (int)(a.BH * qtiles);  // one workgroup per item and chunk
   const dim3 grid((unsigned)items, (unsigned)G);
-  hipLaunchKernelGGL((fa_fwd_lp_pipe_kernel<T, DP, NW, float>), grid, dim3(64 * NW), 0,
-                     a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart,
-                     a.M, a.N, off, qtiles, items, a.c, ks);
+  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, float>, grid, dim3(64 * NW), a.stream,
+                (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart, a.M, a.N, off,
+                qtiles, items, a.c, ks, a.qf);
 }
 
 template <class T, bool CAUSAL>
-void dispatch_lp(const Launch& a) {
+hipError_t dispatch_lp(const Launch& a) {
   if (a.N > 0 && !a.generic) {
     if (a.D == 128) return launch_lp_fast<T, 128, CAUSAL>(a);
     if (a.D == 96) return launch_lp_fast<T, 96, CAUSAL>(a);
     if (a.D == 64) return launch_lp_fast<T, 64, CAUSAL>(a);
   }
-  if (a.D <= 32) launch_lp<T, 32, CAUSAL>(a);
-  else if (a.D <= 64) launch_lp<T, 64, CAUSAL>(a);
-  else if (a.D <= 96) launch_lp<T, 96, CAUSAL>(a);
-  else launch_lp<T, 128, CAUSAL>(a);
+  if (a.D <= 32) return launch_lp<T, 32, CAUSAL>(a);
+  if (a.D <= 64) return launch_lp<T, 64, CAUSAL>(a);
+  if (a.D <= 96) return launch_lp<T, 96, CAUSAL>(a);
+  return launch_lp<T, 128, CAUSAL>(a);
 }
 
 // fp32 with D <= 64 on a grid that would leave most of the GPU idle: split
 // each workgroup's keys over its four waves (four times the workgroups).
 template <int DP, bool CAUSAL>
-void launch_f32_ksplit(const Launch& a) {
+hipError_t launch_f32_ksplit(const Launch& a) {
   const int qtiles = (a.M + 31) / 32;
   const dim3 grid((unsigned)(a.BH * qtiles));
   if (a.D == DP)
-    hipLaunchKernelGGL((fa_fwd_f32_ksplit_kernel<DP, CAUSAL, true>), grid, dim3(NTHREADS), 0,
-                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (float*)a.o, a.lse, a.M, a.N, a.D, qtiles, a.c);
-  else
-    hipLaunchKernelGGL((fa_fwd_f32_ksplit_kernel<DP, CAUSAL, false>), grid, dim3(NTHREADS), 0,
-                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (float*)a.o, a.lse, a.M, a.N, a.D, qtiles, a.c);
+    return launch(fa_fwd_f32_ksplit_kernel<DP, CAUSAL, true>, grid, dim3(NTHREADS), a.stream,
+                  (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.M,
+                  a.N, a.D, qtiles, a.c, a.qf);
+  return launch(fa_fwd_f32_ksplit_kernel<DP, CAUSAL, false>, grid, dim3(NTHREADS), a.stream,
+                (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.M,
+                a.N, a.D, qtiles, a.c, a.qf);
 }
 
 template <bool CAUSAL>
-void dispatch_f32(const Launch& a) {
-  const int cus = device_cus();
+hipError_t dispatch_f32(const Launch& a) {
+  const int cus = device_cus(a.dev);
   if (!a.generic && a.N > 0 && a.D <= 64 && cus > 0 && 2 * (int64_t)a.grid.x < cus) {
     if (a.D <= 32) return launch_f32_ksplit<32, CAUSAL>(a);
     return launch_f32_ksplit<64, CAUSAL>(a);
   }
-  if (a.D <= 32) launch_f32<32, CAUSAL>(a);
-  else if (a.D <= 64) launch_f32<64, CAUSAL>(a);
-  else if (a.D <= 96) launch_f32<96, CAUSAL>(a);
-  else launch_f32<128, CAUSAL>(a);
+  if (a.D <= 32) return launch_f32<32, CAUSAL>(a);
+  if (a.D <= 64) return launch_f32<64, CAUSAL>(a);
+  if (a.D <= 96) return launch_f32<96, CAUSAL>(a);
+  return launch_f32<128, CAUSAL>(a);
 }
 
 // Split-KV partials: chunk g of every head's keys into the fp32 workspace.
 template <class T, int DP, bool CAUSAL>
-void launch_lp_split(const Launch& a, const KeySplit& ks, int G, float* opart, float* lpart) {
+hipError_t launch_lp_split(const Launch& a, const KeySplit& ks, int G, float* opart,
+                           float* lpart) {
   using elt = typename T::elt;
   const dim3 grid(a.grid.x, (unsigned)G);
   if (a.D == DP)
-    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, true, float>), grid, dim3(NTHREADS), 0,
-                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart,
-                       a.M, a.N, a.D, a.qtiles, a.c, ks);
-  else
-    hipLaunchKernelGGL((fa_fwd_lp_kernel<T, DP, CAUSAL, false, float>), grid, dim3(NTHREADS), 0,
-                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart,
-                       a.M, a.N, a.D, a.qtiles, a.c, ks);
+    return launch(fa_fwd_lp_kernel<T, DP, CAUSAL, true, float>, grid, dim3(NTHREADS), a.stream,
+                  (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart, a.M, a.N, a.D,
+                  a.qtiles, a.c, ks, a.qf);
+  return launch(fa_fwd_lp_kernel<T, DP, CAUSAL, false, float>, grid, dim3(NTHREADS), a.stream,
+                (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart, a.M, a.N, a.D,
+                a.qtiles, a.c, ks, a.qf);
 }
 template <int DP, bool CAUSAL>
-void launch_f32_split(const Launch& a, const KeySplit& ks, int G, float* opart, float* lpart) {
+hipError_t launch_f32_split(const Launch& a, const KeySplit& ks, int G, float* opart,
+                            float* lpart) {
   const dim3 grid(a.grid.x, (unsigned)G);
   if (a.D == DP)
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, true>), grid, dim3(NTHREADS), 0, a.stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, opart, lpart, a.M,
-                       a.N, a.D, a.qtiles, a.c, ks);
-  else
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<DP, CAUSAL, false>), grid, dim3(NTHREADS), 0, a.stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, opart, lpart, a.M,
-                       a.N, a.D, a.qtiles, a.c, ks);
+    return launch(fa_fwd_f32_kernel<DP, CAUSAL, true>, grid, dim3(NTHREADS), a.stream,
+                  (const float*)a.q, (const float*)a.k, (const float*)a.v, opart, lpart, a.M, a.N,
+                  a.D, a.qtiles, a.c, ks, a.qf);
+  return launch(fa_fwd_f32_kernel<DP, CAUSAL, false>, grid, dim3(NTHREADS), a.stream,
+                (const float*)a.q, (const float*)a.k, (const float*)a.v, opart, lpart, a.M, a.N,
+                a.D, a.qtiles, a.c, ks, a.qf);
 }
 template <class T, bool CAUSAL>
-void dispatch_lp_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
+hipError_t dispatch_lp_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
   if (a.D == 128) return launch_lp_fast_split<T, 128, CAUSAL>(a, ks, G, op, lp);
   if (a.D == 96) return launch_lp_fast_split<T, 96, CAUSAL>(a, ks, G, op, lp);
   if (a.D == 64) return launch_lp_fast_split<T, 64, CAUSAL>(a, ks, G, op, lp);
-  if (a.D <= 32) launch_lp_split<T, 32, CAUSAL>(a, ks, G, op, lp);
-  else if (a.D <= 64) launch_lp_split<T, 64, CAUSAL>(a, ks, G, op, lp);
-  else if (a.D <= 96) launch_lp_split<T, 96, CAUSAL>(a, ks, G, op, lp);
-  else launch_lp_split<T, 128, CAUSAL>(a, ks, G, op, lp);
+  if (a.D <= 32) return launch_lp_split<T, 32, CAUSAL>(a, ks, G, op, lp);
+  if (a.D <= 64) return launch_lp_split<T, 64, CAUSAL>(a, ks, G, op, lp);
+  if (a.D <= 96) return launch_lp_split<T, 96, CAUSAL>(a, ks, G, op, lp);
+  return launch_lp_split<T, 128, CAUSAL>(a, ks, G, op, lp);
 }
 template <bool CAUSAL>
-void dispatch_f32_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
-  if (a.D <= 32) launch_f32_split<32, CAUSAL>(a, ks, G, op, lp);
-  else if (a.D <= 64) launch_f32_split<64, CAUSAL>(a, ks, G, op, lp);
-  else if (a.D <= 96) launch_f32_split<96, CAUSAL>(a, ks, G, op, lp);
-  else launch_f32_split<128, CAUSAL>(a, ks, G, op, lp);
+hipError_t dispatch_f32_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
+  if (a.D <= 32) return launch_f32_split<32, CAUSAL>(a, ks, G, op, lp);
+  if (a.D <= 64) return launch_f32_split<64, CAUSAL>(a, ks, G, op, lp);
+  if (a.D <= 96) return launch_f32_split<96, CAUSAL>(a, ks, G, op, lp);
+  return launch_f32_split<128, CAUSAL>(a, ks, G, op, lp);
 }
 
-}  // namespace
-
-static int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
-                       int causal, int dtype, void* stream, bool generic) {
-  const int st = fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype);
-  if (st != FA_OK) return st;
-  if (B == 0 || H == 0 || M == 0) return FA_OK;
+// The launch description shared by the entry points (arguments already checked).
+Launch make_launch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                   int64_t H, int64_t M, int64_t N, int64_t D, float scale, int dtype,
+                   void* stream, bool generic) {
   Launch a;
   a.q = q;
   a.k = k;
@@ -1269,25 +1265,41 @@ static int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, flo
   a.N = (int)N;
   a.D = (int)D;
   a.qtiles = (int)((M + BM - 1) / BM);
-  // scale * log2(e) folded once (in double, rounded to fp32) so every exponential is exp2.
-  a.c = (float)((double)scale * 1.4426950408889634074);
+  // scale * log2(e) folded once (in double, rounded to fp32) so every
+  // exponential is exp2; its sign moves into the Q operand (fold_scale).
+  const ScaleFold f = fold_scale(scale, dtype == FA_DTYPE_F32 ? 4 : 2);
+  a.c = f.c;
+  a.qf = f.q;
   a.grid = dim3((unsigned)(B * H * a.qtiles));
   a.BH = B * H;
   a.stream = (hipStream_t)stream;
+  a.dev = stream_device(a.stream);
   a.generic = generic;
-  (void)hipGetLastError();  // clear a stale error so the check below is about this launch
+  return a;
+}
+
+}  // namespace
+
+static int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                       int causal, int dtype, void* stream, bool generic) {
+  const int st = fa_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (B == 0 || H == 0 || M == 0) return FA_OK;
+  const Launch a = make_launch(q, k, v, o, lse, B, H, M, N, D, scale, dtype, stream, generic);
+  hipError_t e;
   switch (dtype) {
     case FA_DTYPE_F16:
-      causal ? dispatch_lp<TF16, true>(a) : dispatch_lp<TF16, false>(a);
+      e = causal ? dispatch_lp<TF16, true>(a) : dispatch_lp<TF16, false>(a);
       break;
     case FA_DTYPE_BF16:
-      causal ? dispatch_lp<TBF16, true>(a) : dispatch_lp<TBF16, false>(a);
+      e = causal ? dispatch_lp<TBF16, true>(a) : dispatch_lp<TBF16, false>(a);
       break;
     default:
-      causal ? dispatch_f32<true>(a) : dispatch_f32<false>(a);
+      e = causal ? dispatch_f32<true>(a) : dispatch_f32<false>(a);
       break;
   }
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1304,8 +1316,62 @@ extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void*
 
 extern "C" int64_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D,
                                               int splits) {
-  if (B < 0 || H < 0 || M < 0 || D < 1 || splits < 1) return -1;
-  return (int64_t)splits * B * H * M * (D + 1) * (int64_t)sizeof(float);
+  if (B < 0 || H < 0 || M < 0 || D < 1 || D > 128 || splits < 1) return -1;
+  int64_t n = (int64_t)splits * (D + 1) * (int64_t)sizeof(float);
+  if (__builtin_mul_overflow(n, B, &n) || __builtin_mul_overflow(n, H, &n) ||
+      __builtin_mul_overflow(n, M, &n))
+    return -1;  // beyond int64: no workspace of that size exists
+  return n;
+}
+
+// The split-KV forward on a workspace of at least fa_splitkv_workspace_bytes
+// (arguments already checked; N > 0).
+static int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                       int causal, int dtype, int splits, void* workspace, void* stream) {
+  // Chunks of ceil(N / splits) keys, rounded up to whole 64-key tiles.
+  int64_t chunk = (N + splits - 1) / splits;
+  chunk = (chunk + 63) / 64 * 64;
+  const int G = (int)((N + chunk - 1) / chunk);
+  const int64_t rows = B * H * M;
+  float* opart = (float*)workspace;
+  float* lpart = opart + (int64_t)G * rows * D;
+  const Launch a = make_launch(q, k, v, o, lse, B, H, M, N, D, scale, dtype, stream, true);
+  const KeySplit ks{(int)chunk, rows * D, rows};
+  hipError_t e;
+  switch (dtype) {
+    case FA_DTYPE_F16:
+      e = causal ? dispatch_lp_split<TF16, true>(a, ks, G, opart, lpart)
+                 : dispatch_lp_split<TF16, false>(a, ks, G, opart, lpart);
+      break;
+    case FA_DTYPE_BF16:
+      e = causal ? dispatch_lp_split<TBF16, true>(a, ks, G, opart, lpart)
+                 : dispatch_lp_split<TBF16, false>(a, ks, G, opart, lpart);
+      break;
+    default:
+      e = causal ? dispatch_f32_split<true>(a, ks, G, opart, lpart)
+                 : dispatch_f32_split<false>(a, ks, G, opart, lpart);
+      break;
+  }
+  if (e != hipSuccess) return FA_ERR_HIP;
+  const int64_t work = rows * ((D + 3) / 4);
+  const int64_t blocks = (work + NTHREADS - 1) / NTHREADS;
+  const dim3 mgrid((unsigned)(blocks < 65536 ? blocks : 65536));
+  switch (dtype) {
+    case FA_DTYPE_F16:
+      e = launch(fa_merge_kernel<_Float16>, mgrid, dim3(NTHREADS), a.stream, (const float*)opart,
+                 (const float*)lpart, (_Float16*)o, lse, rows, (int)D, G, rows * D, rows);
+      break;
+    case FA_DTYPE_BF16:
+      e = launch(fa_merge_kernel<__bf16>, mgrid, dim3(NTHREADS), a.stream, (const float*)opart,
+                 (const float*)lpart, (__bf16*)o, lse, rows, (int)D, G, rows * D, rows);
+      break;
+    default:
+      e = launch(fa_merge_kernel<float>, mgrid, dim3(NTHREADS), a.stream, (const float*)opart,
+                 (const float*)lpart, (float*)o, lse, rows, (int)D, G, rows * D, rows);
+      break;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1318,60 +1384,6 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   if (B == 0 || H == 0 || M == 0) return FA_OK;
   if (N == 0) return fa_fwd_impl(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream,
                                  true);  // every row is empty: no chunk to merge
-  // Chunks of ceil(N / splits) keys, rounded up to whole 64-key tiles.
-  int64_t chunk = (N + splits - 1) / splits;
-  chunk = (chunk + 63) / 64 * 64;
-  const int G = (int)((N + chunk - 1) / chunk);
-  const int64_t rows = B * H * M;
-  float* opart = (float*)workspace;
-  float* lpart = opart + (int64_t)G * rows * D;
-  Launch a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.M = (int)M;
-  a.N = (int)N;
-  a.D = (int)D;
-  a.qtiles = (int)((M + BM - 1) / BM);
-  a.c = (float)((double)scale * 1.4426950408889634074);
-  a.grid = dim3((unsigned)(B * H * a.qtiles));
-  a.BH = B * H;
-  a.stream = (hipStream_t)stream;
-  a.generic = true;
-  const KeySplit ks{(int)chunk, rows * D, rows};
-  (void)hipGetLastError();
-  switch (dtype) {
-    case FA_DTYPE_F16:
-      causal ? dispatch_lp_split<TF16, true>(a, ks, G, opart, lpart)
-             : dispatch_lp_split<TF16, false>(a, ks, G, opart, lpart);
-      break;
-    case FA_DTYPE_BF16:
-      causal ? dispatch_lp_split<TBF16, true>(a, ks, G, opart, lpart)
-             : dispatch_lp_split<TBF16, false>(a, ks, G, opart, lpart);
-      break;
-    default:
-      causal ? dispatch_f32_split<true>(a, ks, G, opart, lpart)
-             : dispatch_f32_split<false>(a, ks, G, opart, lpart);
-      break;
-  }
-  const int64_t work = rows * ((D + 3) / 4);
-  const int64_t blocks = (work + NTHREADS - 1) / NTHREADS;
-  const dim3 mgrid((unsigned)(blocks < 65536 ? blocks : 65536));
-  switch (dtype) {
-    case FA_DTYPE_F16:
-      hipLaunchKernelGGL((fa_merge_kernel<_Float16>), mgrid, dim3(NTHREADS), 0, a.stream, opart,
-                         lpart, (_Float16*)o, lse, rows, (int)D, G, rows * D, rows);
-      break;
-    case FA_DTYPE_BF16:
-      hipLaunchKernelGGL((fa_merge_kernel<__bf16>), mgrid, dim3(NTHREADS), 0, a.stream, opart,
-                         lpart, (__bf16*)o, lse, rows, (int)D, G, rows * D, rows);
-      break;
-    default:
-      hipLaunchKernelGGL((fa_merge_kernel<float>), mgrid, dim3(NTHREADS), 0, a.stream, opart,
-                         lpart, (float*)o, lse, rows, (int)D, G, rows * D, rows);
-      break;
-  }
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return splitkv_run(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, splits, workspace,
+                     stream);
 }

@@ -49,7 +49,7 @@ def run(D, B, H, M, N, causal, seed):
     check(f"{w.name}[head {h}]", dtype, o_h, lse.reshape(B * H, M)[h].cpu().numpy(), O_ref, L_ref)
     s = scale_as_kernel(w.scale)
     rq, rk, rv, parts = oracle.head_bwd(q64, k64, v64, g64, s, causal, return_parts=True)
-    bq, bk, bv = bounds(parts, q64, k64, g64, o_h, s, dtype)
+    bq, bk, bv = bounds(parts, q64, k64, g64, s, dtype)
     for name, got, ref, bnd in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
         check_bwd(f"{w.name}[head {h}] {name}", dtype,
                   got.reshape(B * H, -1, D)[h].double().cpu().numpy(), ref, bnd)

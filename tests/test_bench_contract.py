@@ -64,3 +64,40 @@ def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch)
     assert bench.load_traffic(w, source="fa_bwd.hip") is None  # digest of another file
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
     assert bench.load_traffic(w) is None
+
+
+def test_kernel_label_follows_the_dispatch_rules():
+    """roofline.kernel names what fa_fwd / fa_fwd_splitkv launch: the pipelined
+    kernel for 16-bit D in {64, 96, 128} (split-KV too), else the general or
+    fp32 kernels (the fp32 key-split kernel only for small plain grids)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from workloads import WORKLOADS
+
+    pipe = "fa_fwd_lp_pipe_kernel"
+    w = WORKLOADS["causal_prefill_bf16"]
+    assert bench.fwd_kernel_name(w) == pipe
+    assert bench.fwd_kernel_name(w, splits=4) == pipe + " + fa_merge_kernel (split-KV)"
+    for D in (64, 96):
+        assert bench.fwd_kernel_name(w.with_(D=D), splits=2).startswith(pipe)
+    assert bench.fwd_kernel_name(w.with_(D=100)) == "fa_fwd_lp_kernel"
+    assert bench.fwd_kernel_name(w.with_(D=100), splits=3).startswith("fa_fwd_lp_kernel +")
+    f32 = WORKLOADS["single_head_f32"]
+    assert bench.fwd_kernel_name(f32, cus=256) == "fa_fwd_f32_ksplit_kernel"
+    assert bench.fwd_kernel_name(f32.with_(B=64, H=16), cus=256) == "fa_fwd_f32_kernel"
+    assert bench.fwd_kernel_name(f32, splits=8).startswith("fa_fwd_f32_kernel +")
+
+
+def test_sclk_sampler_parses_the_current_level(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1600Mhz\n2: 2100Mhz *\n3: 2400Mhz\n")
+    s = bench.SclkSampler()
+    s.paths = [str(f)]
+    assert s._read() == 2100.0
+    s.samples = [2100.0, 2000.0, 2200.0]
+    assert s.summary()["median_mhz"] == 2100.0
+    s.paths = [str(tmp_path / "absent")]
+    assert s._read() is None

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
                           "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert fa.fa_abi_version() == 4
+    assert fa.fa_abi_version() == 5
 
 
 def test_status_strings():
@@ -39,22 +39,34 @@ def test_status_strings():
     assert "unknown" in fa.fa_status_string(99)
 
 
-def _chk(**kw):
+FWD_ORDER = ("q", "k", "v", "o", "lse", "B", "H", "M", "N", "D", "scale", "causal", "dtype")
+BWD_ORDER = ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta", "B", "H", "M", "N",
+             "D", "scale", "causal", "dtype")
+SPLIT_ORDER = FWD_ORDER + ("splits", "ws", "wsb")
+
+
+def fwd_args(kw):
+    """fa_check_args' arguments for one table row, in call order."""
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, M=100, N=70, D=64, scale=0.125, causal=0,
              dtype=fa.DTYPE_BF16)
     a.update(kw)
-    return fa.fa_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["M"],
-                            a["N"], a["D"], a["scale"], a["causal"], a["dtype"])
+    return tuple(a[n] for n in FWD_ORDER)
 
 
-@pytest.mark.parametrize("kw,code", [
+def _chk(**kw):
+    return fa.fa_check_args(*fwd_args(kw))
+
+
+FWD_CHECK_CASES = [
     ({}, OK),
     ({"dtype": 3}, DTYPE), ({"dtype": -1}, DTYPE),
     ({"B": -1}, SHAPE), ({"H": -2}, SHAPE), ({"M": -1}, SHAPE), ({"N": -5}, SHAPE),
     ({"causal": 2}, SHAPE),
     ({"D": 0}, BAD_D), ({"D": 129}, BAD_D), ({"D": -3}, BAD_D), ({"D": 1}, OK), ({"D": 128}, OK),
-    ({"scale": 0.0}, SCALE), ({"scale": -0.1}, SCALE), ({"scale": math.inf}, SCALE),
-    ({"scale": math.nan}, SCALE),
+    ({"scale": 0.0}, OK), ({"scale": -0.1}, OK), ({"scale": -1e30}, OK), ({"scale": 1e-45}, OK),
+    ({"scale": 2.3e38}, OK), ({"scale": -2.3e38}, OK),   # scale*log2(e) still finite in fp32
+    ({"scale": 3e38}, SCALE), ({"scale": -3e38}, SCALE),  # scale*log2(e) overflows fp32
+    ({"scale": math.inf}, SCALE), ({"scale": -math.inf}, SCALE), ({"scale": math.nan}, SCALE),
     ({"q": 0}, NULL), ({"o": 0}, NULL), ({"lse": 0}, NULL), ({"k": 0}, NULL), ({"v": 0}, NULL),
     ({"q": P + 8}, ALIGN), ({"k": P + 2}, ALIGN), ({"o": P + 4}, ALIGN), ({"lse": P + 2}, ALIGN),
     ({"lse": P + 4}, OK),
@@ -63,13 +75,22 @@ def _chk(**kw):
     ({"N": 0, "k": 0, "v": 0}, OK),                             # no keys: every row empty
     ({"M": 1 << 25, "D": 64}, LARGE), ({"N": 1 << 25, "D": 64}, LARGE),
     ({"B": 1 << 20, "H": 1 << 12, "M": 128}, LARGE),
-])
+    # int64 edges: M * D, N * D, M + 127, B * H would overflow if formed
+    ({"M": (1 << 63) - 1, "D": 128}, LARGE), ({"N": (1 << 63) - 1, "D": 128}, LARGE),
+    ({"M": (1 << 57), "D": 64}, LARGE), ({"B": (1 << 62), "H": 4}, LARGE),
+    ({"B": (1 << 63) - 1, "H": (1 << 63) - 1, "M": 1}, LARGE),
+    ({"M": (1 << 31) // 64 - 1, "N": (1 << 31) // 64 - 1, "D": 64, "B": 1, "H": 1}, OK),
+    ({"M": (1 << 31) // 64, "D": 64, "B": 1, "H": 1}, LARGE),
+]
+
+
+@pytest.mark.parametrize("kw,code", FWD_CHECK_CASES)
 def test_check_args(kw, code):
     assert _chk(**kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"dtype": 7}, DTYPE), ({"D": 200}, BAD_D), ({"scale": -1.0}, SCALE), ({"q": 0}, NULL),
+    ({"dtype": 7}, DTYPE), ({"D": 200}, BAD_D), ({"scale": math.nan}, SCALE), ({"q": 0}, NULL),
     ({"q": P + 8}, ALIGN), ({"B": 0}, OK), ({"M": 0}, OK),
 ])
 def test_fa_fwd_rejects_before_any_hip_call(kw, code):
@@ -83,21 +104,25 @@ def test_fa_fwd_rejects_before_any_hip_call(kw, code):
     assert st == code
 
 
-def _bchk(**kw):
+def bwd_args(kw):
+    """fa_bwd_check_args' arguments for one table row, in call order."""
     a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, delta=P, B=2, H=3, M=100, N=70,
              D=64, scale=0.125, causal=0, dtype=fa.DTYPE_BF16)
     a.update(kw)
-    return fa.fa_bwd_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
-                                a["dk"], a["dv"], a["delta"], a["B"], a["H"], a["M"], a["N"],
-                                a["D"], a["scale"], a["causal"], a["dtype"])
+    return tuple(a[n] for n in BWD_ORDER)
 
 
-@pytest.mark.parametrize("kw,code", [
+def _bchk(**kw):
+    return fa.fa_bwd_check_args(*bwd_args(kw))
+
+
+BWD_CHECK_CASES = [
     ({}, OK), ({"dtype": fa.DTYPE_F16}, OK),
     ({"dtype": fa.DTYPE_F32}, DTYPE),  # no fp32 backward in this version
     ({"dtype": 3}, DTYPE),
     ({"B": -1}, SHAPE), ({"N": -1}, SHAPE), ({"causal": 2}, SHAPE),
-    ({"D": 0}, BAD_D), ({"D": 129}, BAD_D), ({"scale": 0.0}, SCALE), ({"scale": math.nan}, SCALE),
+    ({"D": 0}, BAD_D), ({"D": 129}, BAD_D), ({"scale": 0.0}, OK), ({"scale": -0.5}, OK),
+    ({"scale": math.nan}, SCALE), ({"scale": 3e38}, SCALE),
     ({"q": 0}, NULL), ({"o": 0}, NULL), ({"lse": 0}, NULL), ({"dout": 0}, NULL), ({"dq": 0}, NULL),
     ({"delta": 0}, NULL), ({"k": 0}, NULL), ({"v": 0}, NULL), ({"dk": 0}, NULL), ({"dv": 0}, NULL),
     ({"dout": P + 8}, ALIGN), ({"dq": P + 2}, ALIGN), ({"dk": P + 4}, ALIGN), ({"dv": P + 8}, ALIGN),
@@ -112,7 +137,12 @@ def _bchk(**kw):
     ({"N": 0, "k": 0, "v": 0, "dk": 0, "dv": 0}, OK),
     ({"M": 1 << 25, "D": 64}, LARGE), ({"N": 1 << 25, "D": 64}, LARGE),
     ({"B": 1 << 20, "H": 1 << 12, "M": 128, "N": 128}, LARGE),
-])
+    ({"M": (1 << 63) - 1, "D": 128}, LARGE), ({"N": (1 << 63) - 1, "D": 96}, LARGE),
+    ({"B": (1 << 63) - 1, "H": (1 << 63) - 1}, LARGE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BWD_CHECK_CASES)
 def test_bwd_check_args(kw, code):
     assert _bchk(**kw) == code
 
@@ -134,28 +164,34 @@ def test_fa_bwd_rejects_before_any_hip_call(kw, code):
 WS = 1 << 20  # a fake 16-byte aligned workspace address
 
 
-def _schk(**kw):
+def split_args(kw):
+    """fa_splitkv_check_args' arguments for one table row, in call order."""
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, M=100, N=70, D=64, scale=0.125, causal=0,
              dtype=fa.DTYPE_BF16, splits=4, ws=WS, wsb=None)
     a.update(kw)
     if a["wsb"] is None:
         a["wsb"] = fa.fa_splitkv_workspace_bytes(a["B"], a["H"], a["M"], a["D"], a["splits"])
-    return fa.fa_splitkv_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
-                                    a["M"], a["N"], a["D"], a["scale"], a["causal"], a["dtype"],
-                                    a["splits"], a["ws"], a["wsb"])
+    return tuple(a[n] for n in SPLIT_ORDER)
+
+
+def _schk(**kw):
+    return fa.fa_splitkv_check_args(*split_args(kw))
 
 
 WORKSPACE = 9
 
 
-@pytest.mark.parametrize("kw,code", [
+SPLIT_CHECK_CASES = [
     ({}, OK), ({"dtype": fa.DTYPE_F32}, OK), ({"splits": 1}, OK), ({"splits": 64}, OK),
     ({"splits": 0}, SHAPE), ({"splits": 65}, SHAPE), ({"splits": -3}, SHAPE),
     ({"ws": 0}, WORKSPACE), ({"ws": WS + 8}, WORKSPACE), ({"wsb": 1000}, WORKSPACE),
-    ({"D": 0}, BAD_D), ({"q": 0}, NULL), ({"scale": -1.0}, SCALE),  # fa_fwd's checks come first
+    ({"D": 0}, BAD_D), ({"q": 0}, NULL), ({"scale": math.inf}, SCALE),  # fa_fwd's checks come first
     ({"N": 0, "k": 0, "v": 0, "ws": 0, "wsb": 0}, OK),  # no keys: no chunk, no workspace needed
     ({"M": 0, "q": 0, "o": 0, "lse": 0, "ws": 0, "wsb": 0}, OK),
-])
+]
+
+
+@pytest.mark.parametrize("kw,code", SPLIT_CHECK_CASES)
 def test_splitkv_check_args(kw, code):
     assert _schk(**kw) == code
 
@@ -165,6 +201,8 @@ def test_splitkv_workspace_bytes():
     assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 1, 1) == 8
     assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 0, 1) == -1
     assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 8, 0) == -1
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 129, 1) == -1
+    assert fa.fa_splitkv_workspace_bytes(1 << 40, 1 << 20, 1 << 10, 128, 64) == -1  # beyond int64
 
 
 def test_fa_fwd_splitkv_rejects_before_any_hip_call():

@@ -9,6 +9,8 @@ import pytest
 import io_aware_tiled_fa_amd as fa
 import oracle
 from oracle.definition import scale_as_kernel
+from gpu_calls import nan_bwd, nan_fwd
+from parity import check as check_fwd
 from parity_bwd import bounds, check
 from workloads import WORKLOADS, Workload, make_dout, make_inputs
 
@@ -24,8 +26,8 @@ def _gpu_fwd_bwd(w, qc, kc, vc, gc):
 
     dev = torch.device("cuda:0")
     q, k, v, g = qc.to(dev), kc.to(dev), vc.to(dev), gc.to(dev)
-    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
-    dq, dk, dv = fa.bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale)
+    o, lse = nan_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = nan_bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -41,6 +43,7 @@ def _check_heads(w, heads=None):
     q64, k64, v64 = (_flat(x.double()).numpy() for x in (qc, kc, vc))
     g64 = _flat(gc.double()).numpy()
     o_gpu = _flat(o.cpu().double()).numpy()
+    l_gpu = _flat(lse.cpu().double()).numpy()
     dq_gpu, dk_gpu, dv_gpu = (_flat(x.cpu().double()).numpy() for x in (dq, dk, dv))
     s = scale_as_kernel(w.scale)
     nh = q64.shape[0]
@@ -49,7 +52,11 @@ def _check_heads(w, heads=None):
     for h in heads:
         rq, rk, rv, parts = oracle.head_bwd(q64[h], k64[h], v64[h], g64[h], s, w.causal,
                                             return_parts=True)
-        bq, bk, bv = bounds(parts, q64[h], k64[h], g64[h], o_gpu[h], s, w.dtype)
+        # the forward output the backward consumes is within the forward's bound,
+        # from which the backward's bound on Delta is derived
+        check_fwd(f"{w.name} head {h} o", w.dtype, o_gpu[h], l_gpu[h], parts["O"], parts["lse"],
+                  verbose=False)
+        bq, bk, bv = bounds(parts, q64[h], k64[h], g64[h], s, w.dtype)
         reps.append(check(f"{w.name} head {h} dq", w.dtype, dq_gpu[h], rq, bq, verbose=False))
         reps.append(check(f"{w.name} head {h} dk", w.dtype, dk_gpu[h], rk, bk, verbose=False))
         reps.append(check(f"{w.name} head {h} dv", w.dtype, dv_gpu[h], rv, bv, verbose=False))
@@ -190,15 +197,17 @@ def test_bwd_tensors_beyond_2_31_elements():
     dev = torch.device("cuda:0")
     q, k, v = make_inputs_device(w, dev)
     g = make_dout_device(w, dev)
-    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
-    dq, dk, dv = fa.bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale)
+    o, lse = nan_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = nan_bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     s = scale_as_kernel(w.scale)
     for h in sorted({0, 2**31 // per - 1, 2**31 // per, w.H - 1}):
         q64, k64, v64, g64 = (x[0, h].double().cpu().numpy() for x in (q, k, v, g))
         o_h = o[0, h].double().cpu().numpy()
         rq, rk, rv, parts = oracle.head_bwd(q64, k64, v64, g64, s, w.causal, return_parts=True)
-        bq, bk, bv = bounds(parts, q64, k64, g64, o_h, s, w.dtype)
+        check_fwd(f"{w.name} head {h} o", w.dtype, o_h, lse[0, h].double().cpu().numpy(),
+                  parts["O"], parts["lse"], verbose=False)
+        bq, bk, bv = bounds(parts, q64, k64, g64, s, w.dtype)
         for name, got, ref, bnd in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
             check(f"{w.name} head {h} {name}", w.dtype, got[0, h].double().cpu().numpy(), ref, bnd)
     del q, k, v, g, o, lse, dq, dk, dv

@@ -8,6 +8,7 @@ import pytest
 
 import io_aware_tiled_fa_amd as fa
 import oracle
+from gpu_calls import nan_fwd
 from parity import TOL_LSE, TOL_O, check
 from workloads import Workload, make_inputs
 
@@ -37,7 +38,7 @@ def _inputs(B, H, M, N, D, dtype, seed, q_mult=1.0):
 def _fwd(q, k, v, causal, scale):
     torch = _t()
     dev = torch.device("cuda:0")
-    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
+    o, lse = nan_fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
     torch.cuda.synchronize()
     return o, lse
 
@@ -221,8 +222,8 @@ def test_fast_and_general_paths_agree(dtype, D, causal):
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     s = 1 / math.sqrt(D)
-    o1, l1 = fa.fwd(qd, kd, vd, causal=causal, scale=s)
-    o2, l2 = fa.fwd(qd, kd, vd, causal=causal, scale=s, general=True)
+    o1, l1 = nan_fwd(qd, kd, vd, causal=causal, scale=s)
+    o2, l2 = nan_fwd(qd, kd, vd, causal=causal, scale=s, general=True)
     torch.cuda.synchronize()
     O_ref, L_ref = oracle.attention(q, k, v, s, causal)
     check(f"fast_{dtype}_D{D}_c{int(causal)}", dtype, o1.double().cpu().numpy(), l1.cpu().numpy(), O_ref, L_ref)
@@ -252,7 +253,7 @@ def test_tensors_beyond_2_31_elements(dtype, D, causal, BH):
     _say(f"{w} ({BH * per} elements per tensor)")
     dev = torch.device("cuda:0")
     q, k, v = make_inputs_device(w, dev)
-    o, lse = fa.fwd(q, k, v, causal=causal, scale=w.scale)
+    o, lse = nan_fwd(q, k, v, causal=causal, scale=w.scale)
     torch.cuda.synchronize()
     elt = 4 if dtype == "f32" else 2
     heads = {0, BH - 1}
@@ -403,3 +404,48 @@ def test_concurrent_streams():
     for i, (a, b) in enumerate(zip(seq, par)):
         for name, x, y in zip(("o", "lse", "dq", "dk", "dv"), a, b):
             assert torch.equal(x, y), f"case {i}: {name} differs between sequential and concurrent runs"
+
+
+def test_caller_error_state_is_kept():
+    """The entry points take their launch status from the launch itself and
+    never call hipGetLastError, so an error the caller has not read yet is still
+    there after fa_fwd, fa_fwd_splitkv and fa_bwd return.  The pending error is
+    an invalid-device hipSetDevice (no GPU work involved)."""
+    import ctypes
+
+    torch = _t()
+    _say("caller error state")
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch and the library share
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in _inputs(1, 2, 100, 130, 64, "bf16", 31))
+    g = torch.randn_like(q)
+    out = torch.empty_like(q)
+    lse = torch.empty(1, 2, 100, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(2, 1, 2, 100, device=dev)
+    ws = torch.empty(fa.fa_splitkv_workspace_bytes(1, 2, 100, 64, 3), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    hip.hipGetLastError()
+    # does this runtime keep an unread error across a successful call?
+    assert hip.hipSetDevice(ctypes.c_int(100000)) != 0
+    n = ctypes.c_int(0)
+    assert hip.hipGetDeviceCount(ctypes.byref(n)) == 0
+    pending = hip.hipPeekAtLastError()
+    if pending == 0:
+        hip.hipGetLastError()
+        pytest.skip("this HIP runtime clears an unread error on the next successful call")
+    stream = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()  # noqa: E731
+    calls = [
+        lambda: fa.fa_fwd(p(q), p(k), p(v), p(out), p(lse), 1, 2, 100, 130, 64, 0.125, 1,
+                          fa.DTYPE_BF16, stream),
+        lambda: fa.fa_fwd_splitkv(p(q), p(k), p(v), p(out), p(lse), 1, 2, 100, 130, 64, 0.125, 1,
+                                  fa.DTYPE_BF16, 3, p(ws), ws.numel(), stream),
+        lambda: fa.fa_bwd(p(q), p(k), p(v), p(out), p(lse), p(g), p(dq), p(dk), p(dv), p(delta),
+                          1, 2, 100, 130, 64, 0.125, 1, fa.DTYPE_BF16, stream),
+    ]
+    for call in calls:
+        assert call() == 0
+        assert hip.hipPeekAtLastError() == pending
+    assert hip.hipGetLastError() == pending
+    torch.cuda.synchronize()
