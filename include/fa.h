@@ -47,7 +47,8 @@ typedef enum {
   FA_ERR_MISALIGNED = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte       */
   FA_ERR_TOO_LARGE = 7,      /* a per-head extent or the grid exceeds the 32-bit limits   */
   FA_ERR_HIP = 8,            /* the HIP runtime reported an error at launch               */
-  FA_ERR_WORKSPACE = 9       /* fa_fwd_splitkv: workspace NULL, misaligned or too small   */
+  FA_ERR_WORKSPACE = 9,      /* fa_fwd_splitkv: workspace NULL, misaligned or too small   */
+  FA_ERR_SCRATCH_LIMIT = 10  /* fa_fwd_splitkv_noalloc: partials exceed FA_NOALLOC_MAX_BYTES */
 } fa_status_t;
 
 /* Largest number of key chunks fa_fwd_splitkv accepts. */
@@ -145,6 +146,30 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  */
 int64_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t M, int64_t D, int splits);
 
+/* Size of the static device scratch behind fa_fwd_splitkv_noalloc (64 MiB). */
+#define FA_NOALLOC_MAX_BYTES ((int64_t)64 << 20)
+
+/*
+ * fa_fwd_splitkv_noalloc - fa_fwd_splitkv for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Arguments, results and errors as fa_fwd_splitkv without `workspace` and
+ * `workspace_bytes`: the fp32 partials go to a file-scope device array of
+ * FA_NOALLOC_MAX_BYTES bytes that each GPU the library runs on holds until the
+ * process ends; its address is looked up once per device, on the first call
+ * that runs there (with that device made current for the lookup).  The call
+ * makes no hipMalloc, hipFree or other allocation.  A problem whose partials,
+ * fa_splitkv_workspace_bytes(B, H, M, D, splits), exceed FA_NOALLOC_MAX_BYTES
+ * returns FA_ERR_SCRATCH_LIMIT and launches nothing.  Every call on one GPU
+ * shares that array and leaves its contents behind (nothing in it needs to
+ * start at zero): calls that may overlap on one GPU, on different streams or
+ * from different threads, race on it and must be ordered by the caller.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                           float scale, int causal, int dtype, int splits, void* stream);
+
 /*
  * fa_splitkv_check_args - the host-side validation fa_fwd_splitkv performs,
  * with its arguments (no stream) and return codes, and no HIP call.
@@ -208,9 +233,9 @@ int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o
 /* fa_status_string - a static, human-readable name for a status code. */
 const char* fa_status_string(int status);
 
-/* fa_abi_version - the ABI revision of this header (currently 5: 3 added fa_bwd
+/* fa_abi_version - the ABI revision of this header (currently 6: 3 added fa_bwd
  * and fa_fwd_splitkv; 4 doubled fa_bwd's workspace to [2, B, H, M]; 5 accepts
- * zero and negative scales). */
+ * zero and negative scales; 6 added fa_fwd_splitkv_noalloc). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,8 @@ import math
 import os
 
 __all__ = ["FaError", "lib_path", "load", "fa_fwd", "fa_fwd_general", "fa_check_args",
-           "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_splitkv_check_args", "fa_bwd",
+           "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_splitkv_check_args",
+           "fa_fwd_splitkv_noalloc", "NOALLOC_MAX_BYTES", "fa_bwd",
            "fa_bwd_check_args", "fa_status_string", "fa_abi_version", "fwd", "bwd", "DTYPE_F32",
            "DTYPE_F16", "DTYPE_BF16", "STATUS", "MAX_SPLITS"]
 
@@ -24,9 +25,10 @@ DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_BAD_DTYPE",
     4: "FA_ERR_UNSUPPORTED_D", 5: "FA_ERR_BAD_SCALE", 6: "FA_ERR_MISALIGNED",
-    7: "FA_ERR_TOO_LARGE", 8: "FA_ERR_HIP", 9: "FA_ERR_WORKSPACE",
+    7: "FA_ERR_TOO_LARGE", 8: "FA_ERR_HIP", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_SCRATCH_LIMIT",
 }
 MAX_SPLITS = 64
+NOALLOC_MAX_BYTES = 64 << 20  # FA_NOALLOC_MAX_BYTES in include/fa.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -64,6 +66,9 @@ def load():
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, vp, i64, vp]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.fa_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.fa_splitkv_workspace_bytes.restype = i64
     lib.fa_splitkv_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, fp,
@@ -104,6 +109,13 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, splits,
     """Direct call of the C entry point; pointers are integer device addresses."""
     return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, M, N, D, float(scale), int(causal),
                                  int(dtype), int(splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, splits,
+                           stream=None) -> int:
+    """Direct call of the allocation-free split-KV entry point (static scratch)."""
+    return load().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, M, N, D, float(scale),
+                                         int(causal), int(dtype), int(splits), stream)
 
 
 def fa_splitkv_workspace_bytes(B, H, M, D, splits) -> int:

@@ -114,8 +114,10 @@ const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
     case FA_ERR_WORKSPACE:
       return "FA_ERR_WORKSPACE: workspace NULL, not 16-byte aligned, or smaller than required";
+    case FA_ERR_SCRATCH_LIMIT:
+      return "FA_ERR_SCRATCH_LIMIT: split-KV partials exceed the static scratch FA_NOALLOC_MAX_BYTES";
     default: return "unknown fa status";
   }
 }
 
-int fa_abi_version(void) { return 5; }
+int fa_abi_version(void) { return 6; }

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa.h"
@@ -1386,4 +1387,49 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
                                  true);  // every row is empty: no chunk to merge
   return splitkv_run(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, splits, workspace,
                      stream);
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV forward without any allocation.  The fp32 partials go to a
+// file-scope device array; in host code its name is only a stand-in for the
+// symbol, so the device address is looked up (hipGetSymbolAddress) once per
+// device, with that device current, and that address is what the kernels get.
+static __device__ __align__(256) char scratch[FA_NOALLOC_MAX_BYTES];
+
+static void* scratch_address(int dev) {
+  static std::mutex mu;
+  static void* addr[64];
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+extern "C" int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                                      int64_t D, float scale, int causal, int dtype, int splits,
+                                      void* stream) {
+  // Host validation with an aligned stand-in for the workspace (never
+  // dereferenced) of the scratch's size: a too-large problem is reported as
+  // the scratch limit, every other error as fa_fwd_splitkv reports it.
+  const int st = fa_splitkv_check_args(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype,
+                                       splits, reinterpret_cast<void*>(256),
+                                       FA_NOALLOC_MAX_BYTES);
+  if (st == FA_ERR_WORKSPACE) return FA_ERR_SCRATCH_LIMIT;
+  if (st != FA_OK) return st;
+  if (B == 0 || H == 0 || M == 0) return FA_OK;
+  if (N == 0) return fa_fwd_impl(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, stream,
+                                 true);  // every row is empty: no partials
+  void* ws = scratch_address(stream_device((hipStream_t)stream));
+  if (ws == nullptr) return FA_ERR_HIP;
+  return splitkv_run(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype, splits, ws, stream);
 }

@@ -27,10 +27,10 @@ def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) >= {"fa_fwd", "fa_check_args", "fa_bwd", "fa_bwd_check_args",
                           "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_splitkv_check_args",
-                          "fa_status_string", "fa_abi_version"}
+                          "fa_status_string", "fa_abi_version", "fa_fwd_splitkv_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
-    assert fa.fa_abi_version() == 5
+    assert fa.fa_abi_version() == 6
 
 
 def test_status_strings():
@@ -203,6 +203,26 @@ def test_splitkv_workspace_bytes():
     assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 8, 0) == -1
     assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 129, 1) == -1
     assert fa.fa_splitkv_workspace_bytes(1 << 40, 1 << 20, 1 << 10, 128, 64) == -1  # beyond int64
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """The allocation-free entry point validates like fa_fwd_splitkv and refuses
+    problems whose partials exceed its static scratch, all on the host."""
+    lim = fa.NOALLOC_MAX_BYTES
+    assert lim == 64 << 20
+    # 2*3*100 rows * 65 * 4 B * 64 splits = 9.98 MB fits; 1024 heads of 512 rows do not
+    assert fa.fa_splitkv_workspace_bytes(2, 3, 100, 64, 64) <= lim
+    big = (1, 1024, 512, 64, 4)
+    assert fa.fa_splitkv_workspace_bytes(*big) > lim
+    assert fa.fa_fwd_splitkv_noalloc(P, P, P, P, P, 1, 1024, 512, 700, 64, 0.125, 1,
+                                     fa.DTYPE_F16, 4, None) == 10
+    assert fa.fa_status_string(10).startswith("FA_ERR_SCRATCH_LIMIT")
+    assert fa.fa_fwd_splitkv_noalloc(P, P, P, P, P, 2, 3, 100, 70, 64, 0.125, 1, fa.DTYPE_F16,
+                                     0, None) == SHAPE
+    assert fa.fa_fwd_splitkv_noalloc(0, P, P, P, P, 2, 3, 100, 70, 64, 0.125, 1, fa.DTYPE_F16,
+                                     4, None) == NULL
+    assert fa.fa_fwd_splitkv_noalloc(P, P, P, P, P, 0, 3, 100, 70, 64, 0.125, 1, fa.DTYPE_F16,
+                                     4, None) == OK
 
 
 def test_fa_fwd_splitkv_rejects_before_any_hip_call():
