@@ -493,9 +493,6 @@ def bench_bwd(args, w):
     import io_aware_tiled_fa_amd as fa
     from workloads import make_dout
 
-    if w.dtype == "f32":
-        print("the backward pass supports fp16 and bf16 workloads", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     log(f"workload {w} (backward)")
     qc, kc, vc = make_inputs(w)
@@ -505,7 +502,7 @@ def bench_bwd(args, w):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((2, w.B, w.H, w.M), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    code = {"f16": fa.DTYPE_F16, "bf16": fa.DTYPE_BF16}[w.dtype]
+    code = {"f32": fa.DTYPE_F32, "f16": fa.DTYPE_F16, "bf16": fa.DTYPE_BF16}[w.dtype]
     ptrs = tuple(t.data_ptr() for t in (q, k, v, o, lse, g, dq, dk, dv, delta))
 
     def step():
@@ -554,7 +551,8 @@ def bench_bwd(args, w):
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": load_traffic(w, key=w.name + "/bwd", source="fa_bwd.hip"),
-            "kernel": "fa_bwd (delta + dkdv + dq kernels, one call)",
+            "kernel": ("fa_bwd (fp32: delta + dkdv + dq kernels on 32x32x2 fp32 MFMA, one call)"
+                       if w.dtype == "f32" else "fa_bwd (delta + dkdv + dq kernels, one call)"),
             "avg_launch_ms": round(avg_launch_ms, 5),
         },
     }

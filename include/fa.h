@@ -203,10 +203,9 @@ int fa_splitkv_check_args(const void* q, const void* k, const void* v, const voi
  *                      for scale 0), 0 where LSE_i = -inf: per-row terms the
  *                      kernels fold into their accumulators)
  *   scale, causal, stream  as for fa_fwd
- *   dtype        FA_DTYPE_F16 or FA_DTYPE_BF16 (FA_DTYPE_F32 returns
- *                FA_ERR_BAD_DTYPE in this version)
- * P and dS are rounded to `dtype` for their matrix products; accumulation is
- * fp32; Delta uses the o passed in.  Written buffers must not overlap each
+ *   dtype        FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16
+ * P and dS are rounded to `dtype` for their matrix products (fp32 inputs keep
+ * them in fp32); accumulation is fp32; Delta uses the o passed in.  Written buffers must not overlap each
  * other or any read buffer.
  *
  * Returns FA_OK once the work is enqueued.  Argument errors are detected on the

@@ -240,7 +240,7 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
     """dq, dk, dv = gradients of fwd's o (with its lse) for the incoming gradient dout.
 
     q [B,H,M,D], k/v [B,H,N,D], o and dout [B,H,M,D] (device tensors of one
-    dtype, float16 or bfloat16), lse [B,H,M] fp32.  Allocates dq, dk, dv and the
+    dtype: float32, float16 or bfloat16), lse [B,H,M] fp32.  Allocates dq, dk, dv and the
     fp32 workspace ``delta`` [2,B,H,M] unless given, enqueues fa_bwd on
     ``stream`` (default: torch's current stream) and returns (dq, dk, dv).
     """

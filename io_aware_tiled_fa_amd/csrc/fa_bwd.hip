@@ -1159,6 +1159,262 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// fp32 backward ("Module 08", "The backward pass: recompute instead of
+// store", for fp32 inputs): the same recomputation on v_mfma_f32_32x32x2f32,
+// with P and dS kept in fp32 (as the fp32 forward keeps P), one workgroup of
+// four waves per (batch*head, 128-key tile) for dK/dV and per (batch*head,
+// 128-query tile) for dQ, 32-row tiles staged through LDS at an odd row
+// stride (conflict-free column reads).
+//
+// Accumulator register r of a 32x32 MFMA tile holds row crow(r, h) of the
+// lane's column (l % 32).  The K = 2 dimension of the fp32 MFMA is split over
+// the two lane halves, so a product summed over the rows of such a tile takes
+// register r of each lane as its B operand for step r (half h contributes row
+// crow(r, h)); the A operand reads the matching rows.
+__device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Per row: ws[row] = -Delta_i = -sum_d dO[i, d] O[i, d] (fp32), and
+// ws[rows + row] = -L_i (unused by the fp32 kernels, kept for the layout).
+__global__ __launch_bounds__(BT) void fa_bwd_delta_f32_kernel(const float* __restrict__ o,
+                                                              const float* __restrict__ dout,
+                                                              const float* __restrict__ lse,
+                                                              float* __restrict__ ws, int64_t rows,
+                                                              int D) {
+  const int sub = threadIdx.x >> 4;
+  const int l16 = threadIdx.x & 15;
+  for (int64_t row0 = (int64_t)blockIdx.x * 16; row0 < rows; row0 += (int64_t)gridDim.x * 16) {
+    const int64_t row = row0 + sub;
+    float acc = 0.0f;
+    if (row < rows)
+      for (int d = l16; d < D; d += 16) acc = __builtin_fmaf(o[row * D + d], dout[row * D + d], acc);
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+    if (row < rows && l16 == 0) {
+      ws[row] = -acc;
+      const float x = lse[row];
+      ws[rows + row] = x == -INFINITY ? 0.0f : -x;
+    }
+  }
+}
+
+// dK and dV, fp32.  Wave w owns keys k0 + 32 w .. + 31; K and V rows stay in
+// registers as the B operands of S = Q K^T and dP = dO V^T (lane: its key,
+// features 2 s + h).
+template <int DP, bool CAUSAL>
+__global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dk, float* __restrict__ dv, int M, int N, int D, int ktiles, float c,
+    float scale, QFold qf) {
+  constexpr int STR = DP + 1;
+  constexpr int KS = DP / 2;
+  constexpr int DT = DP / 32;
+  __shared__ float qs[32 * STR], gs[32 * STR], ls[32], dls[32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<false, BK>(ktiles);
+  const int k0 = tc.q0;
+  const float* Qh = q + (int64_t)tc.bh * M * D;
+  const float* Kh = k + (int64_t)tc.bh * N * D;
+  const float* Vh = v + (int64_t)tc.bh * N * D;
+  const float* Gh = dout + (int64_t)tc.bh * M * D;
+  const float* Lh = lse + (int64_t)tc.bh * M;
+  const float* Dh = delta + (int64_t)tc.bh * M;  // -Delta per row
+  float* dKh = dk + (int64_t)tc.bh * N * D;
+  float* dVh = dv + (int64_t)tc.bh * N * D;
+
+  const int off = N - M;  // causal: key j visible to query i iff j <= i + off
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + l32;
+
+  float kr[KS], vr[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int d = 2 * s + h;
+    const bool in = key < N && d < D;
+    kr[s] = fold_f32(in ? Kh[(int64_t)key * D + d] : 0.0f, qf);
+    vr[s] = in ? Vh[(int64_t)key * D + d] : 0.0f;
+  }
+  f32x16 dka[DT], dva[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dka[dt] = f32x16{};
+    dva[dt] = f32x16{};
+  }
+
+  const int qstart = CAUSAL ? max(0, k0 - off) : 0;
+  for (int qb = qstart / 32 * 32; qb < M; qb += 32) {
+    __syncthreads();  // the previous block's rows are no longer read
+    for (int i = tid; i < 32 * DP; i += BT) {
+      const int r = i / DP;
+      const int d = i - r * DP;
+      const int gq = qb + r;
+      const bool in = gq < M && d < D;
+      qs[r * STR + d] = in ? Qh[(int64_t)gq * D + d] : 0.0f;
+      gs[r * STR + d] = in ? Gh[(int64_t)gq * D + d] : 0.0f;
+    }
+    if (tid < 32) {
+      const int r = qb + tid;
+      // rows past M and rows with no visible key are masked: keep them finite
+      const float x = r < M ? Lh[r] * LOG2E : 0.0f;
+      ls[tid] = x == -INFINITY ? 0.0f : x;
+      dls[tid] = r < M ? Dh[r] : 0.0f;
+    }
+    __syncthreads();
+    // Wave-uniform skip: no query of this block sees any key of this wave.
+    if (kw0 >= N || (CAUSAL && qb + 31 + off < kw0)) continue;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      s = mfma_f32(qs[l32 * STR + 2 * st + h], kr[st], s);
+      dp = mfma_f32(gs[l32 * STR + 2 * st + h], vr[st], dp);
+    }
+    f32x16 p, ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = crow(r, h);
+      const int qi = qb + qr;
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -ls[qr]));
+      const bool vis = qi < M && key < N && (!CAUSAL || key <= qi + off);
+      pr = vis ? pr : 0.0f;
+      p[r] = pr;
+      ds[r] = pr * (dp[r] + dls[qr]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this block.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = crow(r, h);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dva[dt] = mfma_f32(gs[qr * STR + 32 * dt + l32], p[r], dva[dt]);
+        dka[dt] = mfma_f32(qs[qr * STR + 32 * dt + l32], ds[r], dka[dt]);
+      }
+    }
+  }
+
+  if (key < N) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * dt + crow(r, h);
+        if (d < D) {
+          dVh[(int64_t)key * D + d] = dva[dt][r];
+          dKh[(int64_t)key * D + d] = dka[dt][r] * scale;
+        }
+      }
+  }
+}
+
+// dQ, fp32.  Wave w owns queries q0 + 32 w .. + 31; Q and dO rows stay in
+// registers as the B operands of S^T = K Q^T and dP^T = V dO^T.
+template <int DP, bool CAUSAL>
+__global__ __launch_bounds__(BT, 1) void fa_bwd_dq_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dq, int M, int N, int D, int qtiles, float c, float scale, QFold qf) {
+  constexpr int STR = DP + 1;
+  constexpr int KS = DP / 2;
+  constexpr int DT = DP / 32;
+  __shared__ float ks[32 * STR], vs[32 * STR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const TileCoord tc = tile_coord<CAUSAL, BMQ>(qtiles);
+  const int q0 = tc.q0;
+  const float* Qh = q + (int64_t)tc.bh * M * D;
+  const float* Kh = k + (int64_t)tc.bh * N * D;
+  const float* Vh = v + (int64_t)tc.bh * N * D;
+  const float* Gh = dout + (int64_t)tc.bh * M * D;
+  const float* Lh = lse + (int64_t)tc.bh * M;
+  const float* Dh = delta + (int64_t)tc.bh * M;
+  float* dQh = dq + (int64_t)tc.bh * M * D;
+
+  const int off = N - M;
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + l32;
+
+  float qr[KS], gr[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int d = 2 * s + h;
+    const bool in = qrow < M && d < D;
+    qr[s] = fold_f32(in ? Qh[(int64_t)qrow * D + d] : 0.0f, qf);
+    gr[s] = in ? Gh[(int64_t)qrow * D + d] : 0.0f;
+  }
+  float l2 = 0.0f, nd = 0.0f;
+  if (qrow < M) {
+    const float x = Lh[qrow] * LOG2E;
+    l2 = x == -INFINITY ? 0.0f : x;
+    nd = Dh[qrow];
+  }
+  f32x16 dqa[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqa[dt] = f32x16{};
+
+  const int n_end = CAUSAL ? min(N, q0 + BMQ + off) : N;  // keys any row of the workgroup sees
+  const int w_last = min(qw0 + 31, M - 1);
+  for (int kb = 0; kb < n_end; kb += 32) {
+    __syncthreads();
+    for (int i = tid; i < 32 * DP; i += BT) {
+      const int r = i / DP;
+      const int d = i - r * DP;
+      const int gk = kb + r;
+      const bool in = gk < N && d < D;
+      ks[r * STR + d] = in ? Kh[(int64_t)gk * D + d] : 0.0f;
+      vs[r * STR + d] = in ? Vh[(int64_t)gk * D + d] : 0.0f;
+    }
+    __syncthreads();
+    if (qw0 >= M || (CAUSAL && kb > w_last + off)) continue;  // no key of this block visible
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      s = mfma_f32(ks[l32 * STR + 2 * st + h], qr[st], s);
+      dp = mfma_f32(vs[l32 * STR + 2 * st + h], gr[st], dp);
+    }
+    f32x16 ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kj = kb + crow(r, h);
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+      const bool vis = qrow < M && kj < N && (!CAUSAL || kj <= qrow + off);
+      pr = vis ? pr : 0.0f;
+      ds[r] = pr * (dp[r] + nd);
+    }
+    // dQ^T += K^T dS^T over the 32 keys of this block.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr2 = crow(r, h);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dqa[dt] = mfma_f32(ks[kr2 * STR + 32 * dt + l32], ds[r], dqa[dt]);
+    }
+  }
+
+  if (qrow < M) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * dt + crow(r, h);
+        if (d < D) dQh[(int64_t)qrow * D + d] = dqa[dt][r] * scale;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host dispatch.  Every launch returns its own status (see `launch`).
 
 struct BwdArgs {
@@ -1235,6 +1491,44 @@ hipError_t dispatch_full(const BwdArgs& a) {
   return launch_bwd_tiles<T, DP, CAUSAL, false>(a);
 }
 
+template <int DP, bool CAUSAL>
+hipError_t launch_bwd_f32(const BwdArgs& a) {
+  hipError_t e = hipSuccess;
+  if (a.N > 0) {
+    const int ktiles = (a.N + BK - 1) / BK;
+    e = launch(fa_bwd_dkdv_f32_kernel<DP, CAUSAL>, dim3((unsigned)(a.BH * ktiles)), dim3(BT),
+               a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+               (const float*)a.dout, a.lse, (const float*)a.delta, (float*)a.dk, (float*)a.dv, a.M,
+               a.N, a.D, ktiles, a.c, a.scale, a.qf);
+    if (e != hipSuccess) return e;
+  }
+  if (a.M > 0) {
+    const int qtiles = (a.M + BMQ - 1) / BMQ;
+    e = launch(fa_bwd_dq_f32_kernel<DP, CAUSAL>, dim3((unsigned)(a.BH * qtiles)), dim3(BT),
+               a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+               (const float*)a.dout, a.lse, (const float*)a.delta, (float*)a.dq, a.M, a.N, a.D,
+               qtiles, a.c, a.scale, a.qf);
+  }
+  return e;
+}
+
+template <bool CAUSAL>
+hipError_t dispatch_bwd_f32(const BwdArgs& a) {
+  if (a.M > 0) {
+    const int64_t rows = a.BH * a.M;
+    const int64_t blocks = (rows + 15) / 16;
+    const hipError_t e = launch(fa_bwd_delta_f32_kernel,
+                                dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(BT),
+                                a.stream, (const float*)a.o, (const float*)a.dout, a.lse, a.delta,
+                                rows, a.D);
+    if (e != hipSuccess) return e;
+  }
+  if (a.D <= 32) return launch_bwd_f32<32, CAUSAL>(a);
+  if (a.D <= 64) return launch_bwd_f32<64, CAUSAL>(a);
+  if (a.D <= 96) return launch_bwd_f32<96, CAUSAL>(a);
+  return launch_bwd_f32<128, CAUSAL>(a);
+}
+
 template <class T, bool CAUSAL>
 hipError_t dispatch_bwd(const BwdArgs& a) {
   if (a.M > 0) {
@@ -1279,15 +1573,19 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.D = (int)D;
   // The same fp32 constant as the forward pass: exp2(s * c - L * log2 e), with
   // the scale's sign moved into the stationary score operand.
-  const ScaleFold f = fold_scale(scale, 2);
+  const ScaleFold f = fold_scale(scale, dtype == FA_DTYPE_F32 ? 4 : 2);
   a.c = f.c;
   a.s_eff = f.s_eff;
   a.scale = scale;
   a.qf = f.q;
   a.stream = (hipStream_t)stream;
   a.dev = stream_device(a.stream);
-  const hipError_t e = dtype == FA_DTYPE_F16
-                           ? (causal ? dispatch_bwd<TF16, true>(a) : dispatch_bwd<TF16, false>(a))
-                           : (causal ? dispatch_bwd<TBF16, true>(a) : dispatch_bwd<TBF16, false>(a));
+  hipError_t e;
+  if (dtype == FA_DTYPE_F16)
+    e = causal ? dispatch_bwd<TF16, true>(a) : dispatch_bwd<TF16, false>(a);
+  else if (dtype == FA_DTYPE_BF16)
+    e = causal ? dispatch_bwd<TBF16, true>(a) : dispatch_bwd<TBF16, false>(a);
+  else
+    e = causal ? dispatch_bwd_f32<true>(a) : dispatch_bwd_f32<false>(a);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

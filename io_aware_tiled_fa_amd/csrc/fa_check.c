@@ -54,7 +54,6 @@ int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o
                       int64_t N, int64_t D, float scale, int causal, int dtype) {
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
     return FA_ERR_BAD_DTYPE;
-  if (dtype == FA_DTYPE_F32) return FA_ERR_BAD_DTYPE; /* no fp32 backward in this version */
   if (B < 0 || H < 0 || M < 0 || N < 0) return FA_ERR_BAD_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_BAD_SHAPE;
   if (D < 1 || D > 128) return FA_ERR_UNSUPPORTED_D;

@@ -4,7 +4,8 @@ The pages state no accuracy for gradients, so the bound is derived from the
 arithmetic of the kernels, element by element, from exact (oracle) quantities:
 
 * P is rebuilt in fp32 and rounded to the input type (unit roundoff u: 2^-8 for
-  bf16, 2^-11 for fp16) before dV = P^T dO:             |err dV| <= u P^T |dO|
+  bf16, 2^-11 for fp16; fp32 inputs keep P and dS in fp32, u = 2^-24) before
+  dV = P^T dO:                                          |err dV| <= u P^T |dO|
 * Delta uses the forward output the caller passes, which the tests check
   against the forward's own per-element bound |O_gpu - O| <= TOL_O + 1/2 ulp(O)
   (tests/parity.py); so e_D[i] = sum_d |dO_id| (TOL_O + 1/2 ulp(O_id)), from
@@ -26,7 +27,7 @@ import numpy as np
 
 from parity import TOL_O, half_ulp
 
-UNIT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+UNIT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8, "f32": 2.0 ** -24}
 
 
 def bounds(parts: dict, q, k, dout, s: float, dtype: str):

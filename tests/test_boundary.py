@@ -117,8 +117,7 @@ def _bchk(**kw):
 
 
 BWD_CHECK_CASES = [
-    ({}, OK), ({"dtype": fa.DTYPE_F16}, OK),
-    ({"dtype": fa.DTYPE_F32}, DTYPE),  # no fp32 backward in this version
+    ({}, OK), ({"dtype": fa.DTYPE_F16}, OK), ({"dtype": fa.DTYPE_F32}, OK),
     ({"dtype": 3}, DTYPE),
     ({"B": -1}, SHAPE), ({"N": -1}, SHAPE), ({"causal": 2}, SHAPE),
     ({"D": 0}, BAD_D), ({"D": 129}, BAD_D), ({"scale": 0.0}, OK), ({"scale": -0.5}, OK),
@@ -148,7 +147,7 @@ def test_bwd_check_args(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"dtype": fa.DTYPE_F32}, DTYPE), ({"D": 200}, BAD_D), ({"dq": 0}, NULL),
+    ({"dtype": 5}, DTYPE), ({"D": 200}, BAD_D), ({"dq": 0}, NULL),
     ({"dk": P + 8}, ALIGN), ({"B": 0}, OK), ({"M": 0, "N": 0}, OK),
 ])
 def test_fa_bwd_rejects_before_any_hip_call(kw, code):

@@ -97,6 +97,21 @@ SMALL = [
 ]
 
 
+# fp32: P and dS stay fp32 (fa_bwd on v_mfma_f32_32x32x2f32)
+F32 = [
+    _wl("bwd_f32_d64", 1, 2, 100, 150, 64, "f32", False, 3131),
+    _wl("bwd_f32_causal_mgtn_d32", 1, 1, 150, 100, 32, "f32", True, 3132),
+    _wl("bwd_f32_causal_d128", 1, 2, 200, 200, 128, "f32", True, 3133),
+    _wl("bwd_f32_d1", 1, 1, 70, 90, 1, "f32", True, 3134),
+    _wl("bwd_f32_d40_ragged", 1, 1, 130, 257, 40, "f32", False, 3135),
+    _wl("bwd_f32_d65", 1, 1, 64, 64, 65, "f32", True, 3136),
+    _wl("bwd_f32_m1", 1, 1, 1, 300, 96, "f32", False, 3137),
+    _wl("bwd_f32_n1", 1, 1, 300, 1, 64, "f32", False, 3138),
+    _wl("bwd_f32_single_head_shape", 1, 1, 256, 1024, 64, "f32", False, 3139),
+]
+SMALL = SMALL + F32
+
+
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_bwd_small_shapes(w):
     _say(f"{w}")

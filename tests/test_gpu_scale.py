@@ -74,6 +74,7 @@ BWD_PATHS = [
     ("fast_bf16_d128_causal", 1, 2, 300, 260, 128, "bf16", True),
     ("fast_f16_d64", 1, 2, 200, 333, 64, "f16", False),
     ("general_bf16_d40_causal", 1, 2, 130, 200, 40, "bf16", True),
+    ("f32_d64_causal", 1, 2, 200, 260, 64, "f32", True),
 ]
 
 
