@@ -25,6 +25,10 @@
 //    consecutive, which makes the V^T operand one contiguous LDS read.
 //  * exp2 with scale*log2(e) folded into one FMA per score; LSE converted back
 //    to natural log once per row ("FlashAttention-style kernel", "The loop").
+//  * The 16-bit kernels move a row's running max only when a tile raises it by
+//    more than 8 (log2 units); until then p may exceed 1 by up to 2^8.  The
+//    result is the same softmax (the max cancels between O and l, and LSE uses
+//    the max actually subtracted); the accumulator rescale becomes rare.
 //  * Causal (bottom-right, key j visible to row i iff j <= i + N - M): K/V tiles
 //    beyond the workgroup's last visible key are never loaded; a wave skips the
 //    MFMAs of tiles none of its rows can see; masks are applied only on tiles
@@ -121,6 +125,61 @@ __device__ __forceinline__ SoftmaxStep softmax_update(f32x16 (&s)[NT], float c, 
   const bool rescale = __any(m_new > m_run && m_run != -INFINITY);
   m_run = m_new;
   return SoftmaxStep{alpha, rescale};
+}
+
+// Online-softmax update with a lazily moved maximum: the running max m_run of
+// a row moves only when the row's scaled tile max exceeds it by more than
+// LAZY_SLACK (in log2 units), and then to that tile max.  Until then
+// p = exp2(s*c - m_run) may reach 2^LAZY_SLACK, which the fp32 sums and the
+// 16-bit P operand hold without loss; the normalisation by l at the end, and
+// LSE = m + log2(l), do not depend on which max was used.  Each row's maxima
+// depend on its own scores only, so a row's result does not depend on the
+// other rows of its wave.  alpha = exp2(m_old - m_new) is exactly 1 for rows
+// whose max stayed; `grow` (any row of the wave moved) gates the rescale of
+// the accumulator.
+constexpr float LAZY_SLACK = 8.0f;
+struct LazyMax {
+  float m_new, m_use, alpha;
+  bool grow;
+};
+__device__ __forceinline__ LazyMax lazy_max(float mx, float m_run) {
+  const bool up = mx > m_run + LAZY_SLACK;
+  LazyMax r;
+  r.m_new = up ? mx : m_run;
+  r.m_use = (r.m_new == -INFINITY) ? 0.0f : r.m_new;  // nothing visible yet: clamp
+  r.alpha = __builtin_amdgcn_exp2f(m_run - r.m_use);
+  r.grow = __any(up);
+  return r;
+}
+// Sum of 8 values as a fixed tree.
+__device__ __forceinline__ float sum8(const f32x8& p) {
+  return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+// Sum of a lane's 32 p values in the order the pipelined kernel uses: one
+// 8-value tree per P operand chunk (registers 8cc .. 8cc+7), then a tree of the
+// four chunk sums.
+__device__ __forceinline__ float sum_p32(const f32x16 (&s)[2]) {
+  float ps[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    f32x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = s[cc >> 1][8 * (cc & 1) + e];
+    ps[cc] = sum8(pf);
+  }
+  return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+__device__ __forceinline__ SoftmaxStep softmax_update_lazy(f32x16 (&s)[2], float c, float& m_run,
+                                                           float& l_run) {
+  const LazyMax lm = lazy_max(pair_max(max_tree<2>(s)) * c, m_run);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      s[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -lm.m_use));
+  l_run = __builtin_fmaf(l_run, lm.alpha, sum_p32(s));
+  m_run = lm.m_new;
+  return SoftmaxStep{lm.alpha, lm.grow};
 }
 
 // p of a 64-key tile rounded to the 16-bit input type: pb[cc] holds keys
@@ -339,7 +398,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
       }
       const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
       if (need_mask) apply_mask<2>(s, n0, h, lim);
-      const SoftmaxStep st = softmax_update<2>(s, c, m_run, l_run);
+      const SoftmaxStep st = softmax_update_lazy(s, c, m_run, l_run);
       vec8 pb[4];
       pack_p<T>(s, pb);
       if (st.rescale) {
@@ -389,12 +448,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
 // ---------------------------------------------------------------------------
 // Software-pipelined fast path (fp16/bf16, D in {64, 96, 128}).
 //
-// Per wave, tile j's softmax runs while the MFMA unit computes the scores of
-// tile j+1: S(j+1) = K(j+1) Q^T is issued first and its MFMAs are interleaved
-// with the VALU work of softmax(j) (max, exp2, sum, rounding P to 16 bits);
-// then O^T += V(j)^T P(j)^T.  K therefore runs one tile ahead of V, each with
-// its own pair of LDS buffers (same 64 KB as two K+V stages), and the copy
-// of K(j+2) and V(j+1) is in flight during step j.
+// Three tiles are in flight per wave.  Step j issues, on the MFMA unit, the
+// scores of tile j+2 (S(j+2) = K(j+2) Q^T) and the product O^T += V(j)^T P(j)^T,
+// while the VALU computes softmax(j+1) (exp2, row sum, rounding P to 16 bits)
+// and, at the end of the step, the row max of S(j+2).  The step is laid out
+// in slots of two MFMAs with the softmax cut into parts spread over the slots
+// and a scheduling fence after each slot, so that with two waves per SIMD
+// the VALU work of one wave issues under the MFMAs of the other.  K runs two
+// tiles ahead of V; each has a pair of LDS buffers (64 KB at D = 128), and
+// the copies of K(j+3) and V(j+1) are in flight during step j (one barrier
+// per step).  The running max moves lazily (see softmax_update_lazy), so the
+// O rescale is a rare branch instead of DT*16 multiplies per step.
 //
 // One instantiation serves causal and non-causal calls: `off_all` is the
 // causal diagonal offset (key j visible to row i iff j <= i + off_all), N - M
@@ -538,76 +602,144 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     }
   };
 
-  // One step of a wave: softmax(cur) and O += V^T P^T for tile n0, with the
-  // scores of the next tile (into nxt) computed underneath when NEXT.
-  auto body = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[2], f32x16 (&nxt)[2],
-                  const char* kbuf_next, const char* vbuf, int n0) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool NEXT = decltype(next_tag)::value;
-    if (NEXT) s_mfma(nxt, kbuf_next);
-    if (MASK) apply_mask<2>(cur, n0, h, lim);
-    const SoftmaxStep st = softmax_update<2>(cur, c, m_run, l_run);
-    vec8 pb[4];
-    pack_p<T>(cur, pb);
-    if (NEXT) {
-      // Interleave each score MFMA of the next tile with a slice of the softmax
-      // VALU work; K operand reads run four MFMAs ahead.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+  f32x16 sa[2], sb[2];
+  // Three-stage variant: step j computes S(j+2) and O += V(j)^T P(j)^T on the
+  // MFMA unit while the VALU runs softmax(j+1); the VALU work is spread over
+  // all MFMAs of the step.
+  // One step in slots of two MFMAs: NSS score slots (S(j+2), rows 0-31 and
+  // 32-63 of the K tile for one 16-wide slice of d) then 2*DT PV slots.  The
+  // operands of slot s+1 are read from LDS during slot s.  The softmax of
+  // tile j+1 (its row max was taken in the previous step) is cut into parts
+  // spread over the slots; the last two slots take the row max of S(j+2),
+  // whose MFMAs are done by then.  A scheduling fence after each slot keeps
+  // every part, MFMA and LDS read in its slot, so the VALU work of one wave
+  // runs under the MFMAs of the other wave on its SIMD.
+  float mx_next = -INFINITY;  // scaled row max of the next tile to soften
+  auto body3 = [&](auto sm_tag, auto s2_tag, f32x16 (&cur)[2], f32x16 (&nxt)[2],
+                   const vec8 (&p_use)[4], vec8 (&p_make)[4], const char* kbuf_s2,
+                   const char* vbuf, int n2, bool mask_next) __attribute__((always_inline)) {
+    constexpr bool SM = decltype(sm_tag)::value;
+    constexpr bool S2 = decltype(s2_tag)::value;
+    constexpr int NSS = S2 ? KK : 0;
+    constexpr int NSL = NSS + 2 * DT;
+    constexpr int NPART = 10;                    // softmax parts of tile j+1
+    constexpr int NSMSL = S2 ? NSL - 2 : NSL;    // slots that carry them
+    auto load_ops = [&](int sl, vec8 (&o)[2]) __attribute__((always_inline)) {
+      if (sl < NSS) {
+        o[0] = *reinterpret_cast<const vec8*>(kbuf_s2 + koff[sl]);
+        o[1] = *reinterpret_cast<const vec8*>(kbuf_s2 + koff[sl] + 32 * L::ROWB);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 2 * KK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // 10 VALU
-        if (i < 2 * KK - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read
+        for (int u = 0; u < 2; ++u) {
+          const int idx = 2 * (sl - NSS) + u;
+          const int cc = idx / DT, dt = idx % DT;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vbuf + voff[dt] + 16 * cc * L::ROWB));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vbuf + voff[dt] + (16 * cc + 4) * L::ROWB));
+          o[u] = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
-    }
-    if (st.rescale) {
+    };
+    LazyMax lm{};
+    float part_sum[4];
+    auto part = [&](int pi) __attribute__((always_inline)) {
+      if (pi == 0) {
+        lm = lazy_max(mx_next, m_run);
+      } else if (pi < 9) {
+        const int g = pi - 1;  // registers 4g .. 4g+3 of the lane's 32 scores
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= st.alpha;
-    }
+        for (int e = 0; e < 4; ++e) {
+          const int t = g >> 2, r = 4 * (g & 3) + e;
+          cur[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[t][r], c, -lm.m_use));
+        }
+        if (g & 1) {  // registers 8cc .. 8cc+7 are done: P operand cc and its sum
+          const int cc = g >> 1;
+          f32x8 pf;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vbuf + voff[dt] + 16 * cc * L::ROWB));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vbuf + voff[dt] + (16 * cc + 4) * L::ROWB));
-        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[dt] = T::mfma(a, pb[cc], acc[dt]);
+          for (int e = 0; e < 8; ++e) pf[e] = cur[cc >> 1][8 * (cc & 1) + e];
+          p_make[cc] = __builtin_convertvector(pf, vec8);
+          part_sum[cc] = sum8(pf);
+          pin(p_make[cc]);  // computed in this slot, not sunk towards its use
+          pin(part_sum[cc]);
+        } else {
+          pin(cur[g >> 2]);
+        }
+      } else {
+        l_run = __builtin_fmaf(l_run, lm.alpha,
+                               (part_sum[0] + part_sum[1]) + (part_sum[2] + part_sum[3]));
+        m_run = lm.m_new;
       }
+    };
+    vec8 op[2][2];
+    load_ops(0, op[0]);
+    if (S2) {
+      nxt[0] = f32x16{};
+      nxt[1] = f32x16{};
     }
-    // V^T operand reads run two MFMAs ahead of the PV MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    float mxa = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (i < 4 * DT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (sl + 1 < NSL) load_ops(sl + 1, op[(sl + 1) & 1]);
+      const vec8(&o)[2] = op[sl & 1];
+      if (sl < NSS) {
+        nxt[0] = T::mfma(o[0], qreg[sl], nxt[0]);
+        nxt[1] = T::mfma(o[1], qreg[sl], nxt[1]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int idx = 2 * (sl - NSS) + u;
+          acc[idx % DT] = T::mfma(o[u], p_use[idx / DT], acc[idx % DT]);
+        }
+      }
+      if (SM && sl < NSMSL) {
+#pragma unroll
+        for (int pi = (sl * NPART + NSMSL - 1) / NSMSL;
+             pi < ((sl + 1) * NPART + NSMSL - 1) / NSMSL; ++pi)
+          part(pi);
+      }
+      if (S2 && sl == NSL - 2) {
+        if (mask_next) {  // rare: diagonal or N tail; a real branch, not predicated
+          asm volatile("" ::: "memory");
+          apply_mask<2>(nxt, n2, h, lim);
+        }
+        mxa = max_tree16(nxt[0]);
+        pin(mxa);
+      }
+      if (S2 && sl == NSL - 1) {
+        mx_next = pair_max(fmaxf(mxa, max_tree16(nxt[1]))) * c;
+        pin(mx_next);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (SM) pin(l_run);
+    if (SM && lm.grow) {  // rare: some row's max moved by more than the slack
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= lm.alpha;
     }
   };
-
-  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const char* kbuf_next,
-                  const char* vbuf, char* kbuf_load, char* vbuf_load) {
-    if (j + 2 < ntiles) issue(Kh, (j + 2) * BN, kbuf_load, false);
+  auto needs_mask = [&](int n0) { return (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off); };
+  auto step3 = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const vec8 (&p_use)[4],
+                   vec8 (&p_make)[4], const char* kbuf_s2, const char* vbuf, char* kbuf_load,
+                   char* vbuf_load) __attribute__((always_inline)) {
+    if (j + 3 < ntiles) issue(Kh, (j + 3) * BN, kbuf_load, false);
     if (j + 1 < ntiles) issue(Vh, (j + 1) * BN, vbuf_load, true);
     if (j < w_tiles) {
-      const int n0 = j * BN;
-      const bool next = j + 1 < w_tiles;
-      const bool mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
+      const int n2 = (j + 2) * BN;
       using T0 = std::integral_constant<bool, false>;
       using T1 = std::integral_constant<bool, true>;
-      if (!mask) {
-        if (next) body(T0{}, T1{}, cur, nxt, kbuf_next, vbuf, n0);
-        else body(T0{}, T0{}, cur, nxt, kbuf_next, vbuf, n0);
-      } else {
-        if (next) body(T1{}, T1{}, cur, nxt, kbuf_next, vbuf, n0);
-        else body(T1{}, T0{}, cur, nxt, kbuf_next, vbuf, n0);
-      }
+      if (j + 2 < w_tiles)
+        body3(T1{}, T1{}, cur, nxt, p_use, p_make, kbuf_s2, vbuf, n2, needs_mask(n2));
+      else if (j + 1 < w_tiles)
+        body3(T1{}, T0{}, cur, nxt, p_use, p_make, kbuf_s2, vbuf, n2, false);
+      else
+        body3(T0{}, T0{}, cur, nxt, p_use, p_make, kbuf_s2, vbuf, n2, false);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-
-  f32x16 sa[2], sb[2];
+  vec8 pa[4], pb[4];
   if (ntiles > 0) {
     issue(Kh, 0, kb0, false);
     issue(Vh, 0, vb0, true);
@@ -616,11 +748,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (0 < w_tiles) s_mfma(sa, kb0);
+  if (1 < w_tiles) s_mfma(sb, kb1);
   __syncthreads();  // every wave is done reading K(0) before K(2) overwrites it
+  if (ntiles > 2) issue(Kh, 2 * BN, kb0, false);
+  if (0 < w_tiles) {
+    if (needs_mask(0)) apply_mask<2>(sa, 0, h, lim);
+    (void)softmax_update_lazy(sa, c, m_run, l_run);  // acc is still zero
+    pack_p<T>(sa, pa);
+  }
+  if (1 < w_tiles) {
+    if (needs_mask(BN)) apply_mask<2>(sb, BN, h, lim);
+    mx_next = pair_max(max_tree<2>(sb)) * c;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, sa, sb, kb1, vb0, kb0, vb1);
+    step3(j, sb, sa, pa, pb, kb0, vb0, kb1, vb1);
     if (j + 1 >= ntiles) break;
-    step(j + 1, sb, sa, kb0, vb1, kb1, vb0);
+    step3(j + 1, sa, sb, pb, pa, kb1, vb1, kb0, vb0);
   }
 
   const float l_tot = pair_sum(l_run);
