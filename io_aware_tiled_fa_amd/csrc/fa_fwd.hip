@@ -28,7 +28,10 @@
 //  * The 16-bit kernels move a row's running max only when a tile raises it by
 //    more than 8 (log2 units); until then p may exceed 1 by up to 2^8.  The
 //    result is the same softmax (the max cancels between O and l, and LSE uses
-//    the max actually subtracted); the accumulator rescale becomes rare.
+//    the max actually subtracted); the accumulator rescale becomes rare.  Two
+//    row sums are kept: the fp32 sum of p for the LSE, and for O the same sum
+//    with each tile's largest p counted as rounded into the PV operand (that
+//    weight is no longer exactly 1, so its rounding must cancel in O).
 //  * Causal (bottom-right, key j visible to row i iff j <= i + N - M): K/V tiles
 //    beyond the workgroup's last visible key are never loaded; a wave skips the
 //    MFMAs of tiles none of its rows can see; masks are applied only on tiles
@@ -151,6 +154,19 @@ __device__ __forceinline__ LazyMax lazy_max(float mx, float m_run) {
   r.grow = __any(up);
   return r;
 }
+// What rounding the lane's largest p of a tile into the 16-bit PV operand
+// changes it by: p = exp2(lmax * c - m_use) for the lane's raw score maximum
+// lmax, computed exactly as that element's own exponential, minus its
+// rounded value (0 for an all-masked lane).  With a lazily moved max the
+// largest p is up to 2^LAZY_SLACK instead of exactly 1, so its rounding would
+// otherwise bias a peaked row's output; the sum O is normalised by counts the
+// rounded value instead.
+template <class T>
+__device__ __forceinline__ float top_rounding(float lmax, float c, float m_use) {
+  const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(lmax, c, -m_use));
+  return (float)(typename T::elt)p - p;
+}
+
 // Sum of 8 values as a fixed tree.
 __device__ __forceinline__ float sum8(const f32x8& p) {
   return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
@@ -169,15 +185,20 @@ __device__ __forceinline__ float sum_p32(const f32x16 (&s)[2]) {
   }
   return (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
+template <class T>
 __device__ __forceinline__ SoftmaxStep softmax_update_lazy(f32x16 (&s)[2], float c, float& m_run,
-                                                           float& l_run) {
-  const LazyMax lm = lazy_max(pair_max(max_tree<2>(s)) * c, m_run);
+                                                           float& l_run, float& lr_run) {
+  const float lmax = max_tree<2>(s);
+  const LazyMax lm = lazy_max(pair_max(lmax) * c, m_run);
+  const float corr = top_rounding<T>(lmax, c, lm.m_use);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       s[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -lm.m_use));
-  l_run = __builtin_fmaf(l_run, lm.alpha, sum_p32(s));
+  const float ps = sum_p32(s);
+  l_run = __builtin_fmaf(l_run, lm.alpha, ps);
+  lr_run = __builtin_fmaf(lr_run, lm.alpha, ps + corr);
   m_run = lm.m_new;
   return SoftmaxStep{lm.alpha, lm.grow};
 }
@@ -303,6 +324,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY;
   float l_run = 0.0f;
+  float lr_run = 0.0f;  // the sum O is normalised by (see top_rounding)
 
   // Register staging of one K/V tile (global -> registers -> LDS).
   u32x4 kreg[KLD];
@@ -398,7 +420,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
       }
       const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq_first + off);
       if (need_mask) apply_mask<2>(s, n0, h, lim);
-      const SoftmaxStep st = softmax_update_lazy(s, c, m_run, l_run);
+      const SoftmaxStep st = softmax_update_lazy<T>(s, c, m_run, l_run, lr_run);
       vec8 pb[4];
       pack_p<T>(s, pb);
       if (st.rescale) {
@@ -419,9 +441,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
     __syncthreads();
   }
 
-  // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m + log2 l).
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  // Epilogue: O = acc / lr (0 for an empty row), LSE = ln2 * (m + log2 l).
+  const float l_tot = pair_sum(l_run);  // LSE
+  const float lr_tot = pair_sum(lr_run);
+  const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
   if (qrow < M) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -589,6 +612,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY;
   float l_run = 0.0f;
+  float lr_run = 0.0f;  // the sum O is normalised by (see top_rounding)
 
   auto s_mfma = [&](f32x16 (&sx)[2], const char* kbuf) {
     sx[0] = f32x16{};
@@ -615,6 +639,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   // every part, MFMA and LDS read in its slot, so the VALU work of one wave
   // runs under the MFMAs of the other wave on its SIMD.
   float mx_next = -INFINITY;  // scaled row max of the next tile to soften
+  float lmax_next = -INFINITY;  // the lane's raw score max of that tile
   auto body3 = [&](auto sm_tag, auto s2_tag, f32x16 (&cur)[2], f32x16 (&nxt)[2],
                    const vec8 (&p_use)[4], vec8 (&p_make)[4], const char* kbuf_s2,
                    const char* vbuf, int n2, bool mask_next) __attribute__((always_inline)) {
@@ -642,10 +667,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
       }
     };
     LazyMax lm{};
-    float part_sum[4];
+    float part_sum[4], corr = 0.0f;
     auto part = [&](int pi) __attribute__((always_inline)) {
       if (pi == 0) {
         lm = lazy_max(mx_next, m_run);
+        corr = top_rounding<T>(lmax_next, c, lm.m_use);
+        pin(corr);
+        pin(lm.alpha);
       } else if (pi < 9) {
         const int g = pi - 1;  // registers 4g .. 4g+3 of the lane's 32 scores
 #pragma unroll
@@ -666,8 +694,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
           pin(cur[g >> 2]);
         }
       } else {
-        l_run = __builtin_fmaf(l_run, lm.alpha,
-                               (part_sum[0] + part_sum[1]) + (part_sum[2] + part_sum[3]));
+        const float ps = (part_sum[0] + part_sum[1]) + (part_sum[2] + part_sum[3]);
+        l_run = __builtin_fmaf(l_run, lm.alpha, ps);
+        lr_run = __builtin_fmaf(lr_run, lm.alpha, ps + corr);
         m_run = lm.m_new;
       }
     };
@@ -707,12 +736,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
         pin(mxa);
       }
       if (S2 && sl == NSL - 1) {
-        mx_next = pair_max(fmaxf(mxa, max_tree16(nxt[1]))) * c;
+        lmax_next = fmaxf(mxa, max_tree16(nxt[1]));
+        mx_next = pair_max(lmax_next) * c;
         pin(mx_next);
+        pin(lmax_next);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (SM) pin(l_run);
+    if (SM) {
+      pin(l_run);
+      pin(lr_run);
+    }
     if (SM && lm.grow) {  // rare: some row's max moved by more than the slack
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -753,12 +787,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   if (ntiles > 2) issue(Kh, 2 * BN, kb0, false);
   if (0 < w_tiles) {
     if (needs_mask(0)) apply_mask<2>(sa, 0, h, lim);
-    (void)softmax_update_lazy(sa, c, m_run, l_run);  // acc is still zero
+    (void)softmax_update_lazy<T>(sa, c, m_run, l_run, lr_run);  // acc is still zero
     pack_p<T>(sa, pa);
   }
   if (1 < w_tiles) {
     if (needs_mask(BN)) apply_mask<2>(sb, BN, h, lim);
-    mx_next = pair_max(max_tree<2>(sb)) * c;
+    lmax_next = max_tree<2>(sb);
+    mx_next = pair_max(lmax_next) * c;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -768,8 +803,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     step3(j + 1, sa, sb, pb, pa, kb1, vb1, kb0, vb0);
   }
 
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float l_tot = pair_sum(l_run);  // LSE
+  const float lr_tot = pair_sum(lr_run);
+  const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
   if (qrow < M) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
