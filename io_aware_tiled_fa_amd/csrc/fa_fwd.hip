@@ -773,34 +773,120 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  vec8 pa[4], pb[4];
-  if (ntiles > 0) {
-    issue(Kh, 0, kb0, false);
-    issue(Vh, 0, vb0, true);
-  }
-  if (ntiles > 1) issue(Kh, BN, kb1, false);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (0 < w_tiles) s_mfma(sa, kb0);
-  if (1 < w_tiles) s_mfma(sb, kb1);
-  __syncthreads();  // every wave is done reading K(0) before K(2) overwrites it
-  if (ntiles > 2) issue(Kh, 2 * BN, kb0, false);
-  if (0 < w_tiles) {
-    if (needs_mask(0)) apply_mask<2>(sa, 0, h, lim);
-    (void)softmax_update_lazy<T>(sa, c, m_run, l_run, lr_run);  // acc is still zero
-    pack_p<T>(sa, pa);
-  }
-  if (1 < w_tiles) {
-    if (needs_mask(BN)) apply_mask<2>(sb, BN, h, lim);
-    lmax_next = max_tree<2>(sb);
-    mx_next = pair_max(lmax_next) * c;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    step3(j, sb, sa, pa, pb, kb0, vb0, kb1, vb1);
-    if (j + 1 >= ntiles) break;
-    step3(j + 1, sa, sb, pb, pa, kb1, vb1, kb0, vb0);
+  // D = 64: two tiles in flight.  Step j issues the score MFMAs of tile j+1
+  // interleaved (scheduling hints) with softmax(j)'s VALU work, then the PV
+  // MFMAs of tile j; K runs one tile ahead of V.  At D = 64 the VALU work per
+  // MFMA is twice that of D = 128 and, with two workgroups per CU whose waves
+  // are not in step, this measured faster than the three-tile slots.
+  auto body2 = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[2], f32x16 (&nxt)[2],
+                   const char* kbuf_next, const char* vbuf, int n0) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    if (NEXT) s_mfma(nxt, kbuf_next);
+    if (MASK) apply_mask<2>(cur, n0, h, lim);
+    const SoftmaxStep st = softmax_update_lazy<T>(cur, c, m_run, l_run, lr_run);
+    vec8 pb2[4];
+    pack_p<T>(cur, pb2);
+    if (NEXT) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+#pragma unroll
+      for (int i = 0; i < 2 * KK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // 10 VALU
+        if (i < 2 * KK - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read
+      }
+    }
+    if (st.rescale) {  // rare: some row's max moved by more than the slack
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= st.alpha;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vbuf + voff[dt] + 16 * cc * L::ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vbuf + voff[dt] + (16 * cc + 4) * L::ROWB));
+        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = T::mfma(a, pb2[cc], acc[dt]);
+      }
+    }
+    // V^T operand reads run two MFMAs ahead of the PV MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (i < 4 * DT - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+  };
+  auto step2 = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], const char* kbuf_next,
+                   const char* vbuf, char* kbuf_load, char* vbuf_load) __attribute__((always_inline)) {
+    if (j + 2 < ntiles) issue(Kh, (j + 2) * BN, kbuf_load, false);
+    if (j + 1 < ntiles) issue(Vh, (j + 1) * BN, vbuf_load, true);
+    if (j < w_tiles) {
+      const int n0 = j * BN;
+      const bool next = j + 1 < w_tiles;
+      using T0 = std::integral_constant<bool, false>;
+      using T1 = std::integral_constant<bool, true>;
+      if (!needs_mask(n0)) {
+        if (next) body2(T0{}, T1{}, cur, nxt, kbuf_next, vbuf, n0);
+        else body2(T0{}, T0{}, cur, nxt, kbuf_next, vbuf, n0);
+      } else {
+        if (next) body2(T1{}, T1{}, cur, nxt, kbuf_next, vbuf, n0);
+        else body2(T1{}, T0{}, cur, nxt, kbuf_next, vbuf, n0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if constexpr (DP == 64) {
+    if (ntiles > 0) {
+      issue(Kh, 0, kb0, false);
+      issue(Vh, 0, vb0, true);
+    }
+    if (ntiles > 1) issue(Kh, BN, kb1, false);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (0 < w_tiles) s_mfma(sa, kb0);
+    __syncthreads();  // every wave is done reading K(0) before K(2) overwrites it
+    for (int j = 0; j < ntiles; j += 2) {
+      step2(j, sa, sb, kb1, vb0, kb0, vb1);
+      if (j + 1 >= ntiles) break;
+      step2(j + 1, sb, sa, kb0, vb1, kb1, vb0);
+    }
+  } else {
+    vec8 pa[4], pb[4];
+    if (ntiles > 0) {
+      issue(Kh, 0, kb0, false);
+      issue(Vh, 0, vb0, true);
+    }
+    if (ntiles > 1) issue(Kh, BN, kb1, false);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (0 < w_tiles) s_mfma(sa, kb0);
+    if (1 < w_tiles) s_mfma(sb, kb1);
+    __syncthreads();  // every wave is done reading K(0) before K(2) overwrites it
+    if (ntiles > 2) issue(Kh, 2 * BN, kb0, false);
+    if (0 < w_tiles) {
+      if (needs_mask(0)) apply_mask<2>(sa, 0, h, lim);
+      (void)softmax_update_lazy<T>(sa, c, m_run, l_run, lr_run);  // acc is still zero
+      pack_p<T>(sa, pa);
+    }
+    if (1 < w_tiles) {
+      if (needs_mask(BN)) apply_mask<2>(sb, BN, h, lim);
+      lmax_next = max_tree<2>(sb);
+      mx_next = pair_max(lmax_next) * c;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int j = 0; j < ntiles; j += 2) {
+      step3(j, sb, sa, pa, pb, kb0, vb0, kb1, vb1);
+      if (j + 1 >= ntiles) break;
+      step3(j + 1, sa, sb, pb, pa, kb1, vb1, kb0, vb0);
+    }
   }
 
   const float l_tot = pair_sum(l_run);  // LSE
