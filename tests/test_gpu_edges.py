@@ -449,3 +449,46 @@ def test_caller_error_state_is_kept():
         assert hip.hipPeekAtLastError() == pending
     assert hip.hipGetLastError() == pending
     torch.cuda.synchronize()
+
+
+def _profiled_inputs(M, N, D, dtype, profile, seed):
+    """Q, K, V whose scaled scores c*s_ij follow a chosen profile over the keys
+    for every row (up to a per-row factor near 1): Q rows share a common
+    direction g, and key j is a_j * g / |g|^2 plus small noise."""
+    torch = _t()
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(D)
+    c = scale * math.log2(math.e)
+    j = np.arange(N)
+    a = {"ramp": 3.0 * j / 64,                       # the max rises by ~3 per 64-key tile
+         "steps8": 8.0 * (j // 64) + 0.1 * rng.standard_normal(N),  # ~8 per tile: the slack
+         "spike": 0.5 * rng.standard_normal(N) + np.where(j == (3 * N) // 4, 40.0, 0.0),
+         "falling": 20.0 - 3.0 * j / 64}[profile] / c
+    g = rng.standard_normal(D)
+    g *= 4.0 / np.linalg.norm(g)
+    q = g[None, :] + 0.05 * rng.standard_normal((M, D))
+    k = a[:, None] * (g / (g @ g))[None, :] + 0.02 * rng.standard_normal((N, D))
+    v = rng.standard_normal((N, D))
+    tdt = _dt(dtype)
+    cast = lambda x: torch.from_numpy(x[None, None].astype(np.float32)).to(tdt)  # noqa: E731
+    return cast(q), cast(k), cast(v), scale
+
+
+@pytest.mark.parametrize("profile", ["ramp", "steps8", "spike", "falling"])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 96), ("f16", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_profiles(profile, dtype, D, causal):
+    """Score profiles that move the running row max in every way the 16-bit
+    kernels treat differently: a steady rise (the reference max trails the
+    row max by up to the slack), rises of about the slack per tile, one late
+    spike far above everything (the accumulator rescale), and a max reached in
+    the first tile.  Checked against the oracle with no element above the
+    bare tolerance (|O| stays well below 4 here)."""
+    M = N = 512
+    _say(f"max profile={profile} dtype={dtype} D={D} causal={causal}")
+    q, k, v, s = _profiled_inputs(M, N, D, dtype, profile, 1700 + D)
+    o, lse = _fwd(q, k, v, causal, s)
+    O_ref, L_ref = oracle.attention(q, k, v, s, causal)
+    rep = check(f"maxprofile_{profile}_{dtype}_D{D}_c{int(causal)}", dtype,
+                o.double().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref)
+    assert rep["o_above_bare_tol"] == 0, rep
