@@ -59,6 +59,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_info():
+    """CPU model and BLAS library the oracle's timing ran with."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(libs)
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
 def cpu_baseline(w, qc, kc, vc, budget_s: float = 15.0, max_heads: int = 1 << 30):
     """Time the fp64 oracle on whole heads of the workload until ~budget_s."""
     import numpy as np
@@ -92,6 +116,7 @@ def cpu_baseline(w, qc, kc, vc, budget_s: float = 15.0, max_heads: int = 1 << 30
         "kind": "oracle",
         "sample": f"{done} of {w.B * w.H} heads, all {w.M} rows, fp64 numpy, "
                   f"{dt:.1f} s wall ({os.cpu_count()} cpus visible)",
+        **host_info(),
     }
 
 
@@ -124,6 +149,7 @@ def cpu_baseline_bwd(w, qc, kc, vc, gc, budget_s: float = 15.0):
         "kind": "oracle",
         "sample": f"{done} of {w.B * w.H} heads, all {w.M} rows, fp64 numpy backward, "
                   f"{dt:.1f} s wall ({os.cpu_count()} cpus visible)",
+        **host_info(),
     }
 
 

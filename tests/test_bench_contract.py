@@ -40,6 +40,7 @@ def test_bench_prints_one_contract_line():
     assert 0 < rl["frac"] < 1 and abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["cpu_model"] and cb["blas"]
 
 
 def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
