@@ -1094,13 +1094,23 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
       }
     }
     const bool need_mask = (n0 + 64 > N) || (n0 + 63 > wq_first + off);
+    if (need_mask) {  // rare: diagonal or N tail.  Masked scores become -inf
+      // (P = 0).  The scores pass through an opaque statement first, so that
+      // the selects stay inside this branch instead of running on every tile.
+      pin(s[0]);
+      pin(s[1]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[t][r] = n0 + 32 * t + key_of_reg(r, h) < lim ? s[t][r] : -INFINITY;
+    }
     f32x16 ds[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -l2));
-        if (need_mask) pr = (n0 + 32 * t + key_of_reg(r, h) < lim) ? pr : 0.0f;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -l2));
         ds[t][r] = pr * (dp[t][r] - dl);
       }
     vec8 dsb[4];
