@@ -337,16 +337,18 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_kernel(
       const bool need_mask = (qb + 31 >= M) || (kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qb + off);
       f32x16 p, ds;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
-        if (need_mask) {
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
+      if (need_mask) {  // rare: a real branch (P is pinned first so the selects stay in it);
+        pin(p);         // rows with L = -inf have no visible key and are masked here
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int qi = qb + key_of_reg(r, h);
           const bool vis = qi < M && key < N && (!CAUSAL || key <= qi + off);
-          pr = vis ? pr : 0.0f;
+          p[r] = vis ? p[r] : 0.0f;
         }
-        p[r] = pr;
-        ds[r] = pr * (dp[r] - dl[r]);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[r] - dl[r]);
       vec8 pb[2], dsb[2];
       pack16<T>(p, pb);
       pack16<T>(ds, dsb);
@@ -914,13 +916,21 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
         }
       }
       const bool need_mask = (n0 + BNK > N) || (CAUSAL && n0 + BNK - 1 > wq_first + off);
+      if (need_mask) {  // rare: masked scores become -inf (P = 0); see fa_bwd_dq_fast_kernel
+        pin(s[0]);
+        pin(s[1]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[t][r] = n0 + 32 * t + key_of_reg(r, h) < lim ? s[t][r] : -INFINITY;
+      }
       f32x16 ds[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -l2));
-          if (need_mask) pr = (n0 + 32 * t + key_of_reg(r, h) < lim) ? pr : 0.0f;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -l2));
           ds[t][r] = pr * (dp[t][r] - dl);
         }
       vec8 dsb[4];
