@@ -488,13 +488,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fa_fwd_lp_kernel(
 // for a bottom-right causal mask and N for no mask (no row can reach it, so
 // only the N tail is ever masked).  With a key split (blockIdx.y = chunk) the
 // same offset, less the chunk's first key, applies to the chunk's keys.
-template <class T, int DP, int NW, class OUT>
+//
+// PAD: the rows hold Drow < DP features, Drow a multiple of 8, so every row is
+// a whole number of 16-byte chunks and starts 16-byte aligned.  Chunks at or
+// past Drow are neither loaded nor copied: Q's are zero in registers, K's and
+// V's stay zero in LDS (cleared once at the start), so they add nothing to the
+// scores and only fill output columns that are not stored.
+template <class T, int DP, int NW, class OUT, bool PAD>
 __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, OUT* __restrict__ o, float* __restrict__ lse, int M,
-    int Ntot, int off_all, int qtiles, int items, float c, KeySplit ks, QFold qf) {
+    int Ntot, int off_all, int qtiles, int items, float c, KeySplit ks, QFold qf, int Drow) {
   constexpr bool CAUSAL = true;  // masking logic always on; `off` decides what it masks
-  constexpr int D = DP;          // the dispatcher routes only D == DP here
+  const int D = PAD ? Drow : DP;  // features per row in HBM
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using L = FastLayout<DP>;
@@ -514,6 +520,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
+
+  if constexpr (PAD) {  // padding chunks of all four tile buffers read as zeros
+    constexpr int NB = L::TILEB / 16;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < NB; i += 64 * NW) {
+      *reinterpret_cast<u32x4*>(kb0 + 16 * i) = z;
+      *reinterpret_cast<u32x4*>(kb1 + 16 * i) = z;
+      *reinterpret_cast<u32x4*>(vb0 + 16 * i) = z;
+      *reinterpret_cast<u32x4*>(vb1 + 16 * i) = z;
+    }
+    __syncthreads();
+  }
 
   // Persistent loop (8-wave instantiations, one workgroup per CU): with fewer
   // workgroups than work items a workgroup takes several items, one after the
@@ -548,7 +566,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qrow < M) raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * kk + 8 * h);
+    if (qrow < M && (!PAD || 16 * kk + 8 * h < D))
+      raw = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * kk + 8 * h);
     qreg[kk] = __builtin_bit_cast(vec8, fold_bits(raw, qf));
   }
 
@@ -570,7 +589,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
   const int lds_w = __builtin_amdgcn_readfirstlane(w * 1024);  // wave-uniform LDS offset
   auto issue = [&](const elt* src, int n0, char* buf, bool is_v) {
     const int chunk = is_v ? chunk_v : chunk_k;
-    if (chunk >= L::CPR) return;  // D = 96: slots 12..15 of a row hold no data
+    if (chunk >= L::CPR) return;       // D = 96: slots 12..15 of a row hold no data
+    if (PAD && 8 * chunk >= D) return;  // padding: stays zero
     const unsigned goff = is_v ? goff_v : goff_k;
     if (n0 + BN <= N) {
       const char* base = reinterpret_cast<const char*>(src + (int64_t)n0 * D);
@@ -901,7 +921,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd_lp_pipe_kernel(
         OUT y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = (OUT)(acc[dt][4 * g + e] * inv);
-        store4<OUT>(Oh + (int64_t)qrow * D + d0, y);
+        if (!PAD || d0 < D) store4<OUT>(Oh + (int64_t)qrow * D + d0, y);
       }
     if (h == 0)
       Lh[qrow] = l_tot > 0.0f ? LN2F * (m_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
@@ -1382,8 +1402,11 @@ hipError_t launch_f32(const Launch& a) {
 // measured faster; at D = 64 the 128-row workgroup (two per CU) is faster.
 template <int DP>
 constexpr int fast_waves() { return DP == 64 ? 4 : 8; }
+// Smallest D of the padded fast path: at or below it the padded work of the
+// 64-wide kernel costs more than the general kernel's register staging.
+constexpr int PAD_MIN_D = 32;
 
-template <class T, int DP, bool CAUSAL, int NW>
+template <class T, int DP, bool CAUSAL, int NW, bool PAD>
 hipError_t launch_lp_fast_nw(const Launch& a) {
   using elt = typename T::elt;
   const int off = CAUSAL ? a.N - a.M : a.N;
@@ -1395,27 +1418,27 @@ hipError_t launch_lp_fast_nw(const Launch& a) {
   // Only the 8-wave kernel loops over items; a 4-wave launch has one per item.
   int slots = 0;
   if constexpr (NW == 8)
-    slots = persistent_workgroups<fa_fwd_lp_pipe_kernel<T, DP, NW, elt>>(64 * NW, a.dev);
+    slots = persistent_workgroups<fa_fwd_lp_pipe_kernel<T, DP, NW, elt, PAD>>(64 * NW, a.dev);
   const int P = slots >= NXCD && slots < items ? slots : items;
   const KeySplit ks{a.N, 0, 0};
-  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, elt>, dim3((unsigned)P), dim3(64 * NW), a.stream,
-                (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M, a.N, off,
-                qtiles, items, a.c, ks, a.qf);
+  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, elt, PAD>, dim3((unsigned)P), dim3(64 * NW),
+                a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, (elt*)a.o, a.lse, a.M,
+                a.N, off, qtiles, items, a.c, ks, a.qf, (int)a.D);
 }
 
 // At D = 96 and 128, when even 128-row workgroups (twice as many) leave a CU
 // for each, the grid runs on those: the same work on twice the CUs.  (Where
 // the doubled grid would put two workgroups on some CUs it measured slower.)
-template <class T, int DP, bool CAUSAL>
+template <class T, int DP, bool CAUSAL, bool PAD>
 hipError_t launch_lp_fast(const Launch& a) {
   constexpr int NW = fast_waves<DP>();
   if constexpr (NW == 8) {
     const int64_t wide = a.BH * ((a.M + 32 * NW - 1) / (32 * NW));
     const int cus = device_cus(a.dev);
     if (cus > 0 && a.BH * ((a.M + 127) / 128) <= cus && wide < cus)
-      return launch_lp_fast_nw<T, DP, CAUSAL, 4>(a);
+      return launch_lp_fast_nw<T, DP, CAUSAL, 4, PAD>(a);
   }
-  return launch_lp_fast_nw<T, DP, CAUSAL, NW>(a);
+  return launch_lp_fast_nw<T, DP, CAUSAL, NW, PAD>(a);
 }
 
 // Split-KV partials on the fast path (fp32 outputs into the workspace).
@@ -1429,17 +1452,24 @@ hipError_t launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, floa
   const int qtiles = (a.M + rows - 1) / rows;
   const int items = (int)(a.BH * qtiles);  // one workgroup per item and chunk
   const dim3 grid((unsigned)items, (unsigned)G);
-  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, float>, grid, dim3(64 * NW), a.stream,
+  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, float, false>, grid, dim3(64 * NW), a.stream,
                 (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart, a.M, a.N, off,
-                qtiles, items, a.c, ks, a.qf);
+                qtiles, items, a.c, ks, a.qf, DP);
 }
 
 template <class T, bool CAUSAL>
 hipError_t dispatch_lp(const Launch& a) {
   if (a.N > 0 && !a.generic) {
-    if (a.D == 128) return launch_lp_fast<T, 128, CAUSAL>(a);
-    if (a.D == 96) return launch_lp_fast<T, 96, CAUSAL>(a);
-    if (a.D == 64) return launch_lp_fast<T, 64, CAUSAL>(a);
+    if (a.D == 128) return launch_lp_fast<T, 128, CAUSAL, false>(a);
+    if (a.D == 96) return launch_lp_fast<T, 96, CAUSAL, false>(a);
+    if (a.D == 64) return launch_lp_fast<T, 64, CAUSAL, false>(a);
+    // Other multiples of 8 above 32 run the fast kernel of the next size up
+    // with zero padding (PAD_MIN_D and below stay on the general kernel).
+    if (a.D % 8 == 0 && a.D > PAD_MIN_D) {
+      if (a.D < 64) return launch_lp_fast<T, 64, CAUSAL, true>(a);
+      if (a.D < 96) return launch_lp_fast<T, 96, CAUSAL, true>(a);
+      return launch_lp_fast<T, 128, CAUSAL, true>(a);
+    }
   }
   if (a.D <= 32) return launch_lp<T, 32, CAUSAL>(a);
   if (a.D <= 64) return launch_lp<T, 64, CAUSAL>(a);
