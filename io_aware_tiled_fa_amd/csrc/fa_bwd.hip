@@ -483,19 +483,25 @@ __device__ __forceinline__ void lds_copy_tile(const void* qb, const void* gb, co
   }
 }
 
-template <class T, int DP, int NBUF>
+//
+// PAD: the rows hold Drow < DP features, Drow a multiple of 8 (whole 16-byte
+// chunks, 16-byte aligned rows).  Chunks at or past Drow are neither loaded nor
+// copied: K's and V's are zero in registers, Q's and dO's stay zero in LDS
+// (cleared once at the start), so they add nothing to S and dP and only fill
+// gradient columns that are not stored.
+template <class T, int DP, int NBUF, bool PAD>
 __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dk,
     typename T::elt* __restrict__ dv, int M, int N, int ktiles, int items, float c, float scale,
-    int causal, QFold qf) {
+    int causal, QFold qf, int Drow) {
   // lse is unused here: `delta` points at the workspace [2, B*H*M], whose
   // second half holds -L / scale per row (see fa_bwd_delta_kernel).
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using L = FastLayout<DP>;
-  constexpr int D = DP;
+  const int D = PAD ? Drow : DP;  // features per row in HBM
   constexpr int KK = DP / 16;
   constexpr int DT = DP / 32;
   constexpr int NW = BT / 64;
@@ -516,6 +522,12 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
+
+  if constexpr (PAD) {  // padding chunks of the Q and dO buffers read as zeros
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < NBUF * BUFB / 16; i += BT) *reinterpret_cast<u32x4*>(lds + 16 * i) = z;
+    __syncthreads();
+  }
 
   // Persistent loop at D >= 96 (one workgroup per CU): items are
   // (batch*head, key tile), key tiles in natural order (under the causal mask
@@ -571,7 +583,8 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     const int b = qt % NBUF;
     const int q0 = qt * BQ;
     const unsigned dst = lds_w + (unsigned)(b * BUFB);
-    if (chunk < L::CPR) {  // D = 96: slots 12..15 of a row hold no data
+    // D = 96: slots 12..15 of a row hold no data; padding chunks stay zero
+    if (chunk < L::CPR && (!PAD || 8 * chunk < D)) {
       // Byte offsets within the head (M * D < 2^31 elements, so they fit 32 bits).
       unsigned off[BPW];
       const unsigned off0 = (unsigned)((q0 + cp_row) * D * 2 + 16 * chunk);
@@ -766,8 +779,9 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     if (qt0 + i < nqt) issue(qt0 + i);
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    kb[kk] = fold_vec(load_row8<T, true>(Kh, key, N, D, 16 * kk + 8 * h), qf);
-    vb[kk] = load_row8<T, true>(Vh, key, N, D, 16 * kk + 8 * h);
+    const bool in_d = !PAD || 16 * kk + 8 * h < D;  // padding chunks: zero
+    kb[kk] = fold_vec(load_row8<T, true>(Kh, in_d ? key : N, N, D, 16 * kk + 8 * h), qf);
+    vb[kk] = load_row8<T, true>(Vh, in_d ? key : N, N, D, 16 * kk + 8 * h);
   }
   if (qt0 < nqt) {
     wait_copies(min(NBUF - 2, nqt - 1 - qt0));
@@ -800,6 +814,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dt + 8 * g + 4 * h;
+        if (PAD && d0 >= D) continue;  // padding columns
         store_row4<T, true>(dVh, key, D, d0, dva[dt], g, 1.0f);
         store_row4<T, true>(dKh, key, D, d0, dka[dt], g, scale);
       }
@@ -971,16 +986,18 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dq_kernel(
 // K-operand swizzle of FastLayout, which keeps the row reads of S^T = K Q^T and
 // dP^T = V dO^T and the transposing reads of K^T (for dQ^T += K^T dS^T)
 // bank-conflict free.
-template <class T, int DP, int NW>
+// PAD: Drow < DP features per row, as in the fast dK/dV kernel (Q and dO
+// padding zero in registers, K and V padding zero in LDS).
+template <class T, int DP, int NW, bool PAD>
 __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
     const typename T::elt* __restrict__ q, const typename T::elt* __restrict__ k,
     const typename T::elt* __restrict__ v, const typename T::elt* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, typename T::elt* __restrict__ dq,
-    int M, int N, int qtiles, int items, float c, float scale, int causal, QFold qf) {
+    int M, int N, int qtiles, int items, float c, float scale, int causal, QFold qf, int Drow) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
   using L = FastLayout<DP>;
-  constexpr int D = DP;
+  const int D = PAD ? Drow : DP;  // features per row in HBM
   constexpr int KK = DP / 16;
   constexpr int DT = DP / 32;
   constexpr int BPW = L::NBLK / NW;
@@ -997,6 +1014,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
+
+  if constexpr (PAD) {  // padding chunks of the K and V buffers read as zeros
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < L::TILEB / 16; i += 64 * NW) {
+      *reinterpret_cast<u32x4*>(kb0 + 16 * i) = z;
+      *reinterpret_cast<u32x4*>(kb1 + 16 * i) = z;
+      *reinterpret_cast<u32x4*>(vb0 + 16 * i) = z;
+      *reinterpret_cast<u32x4*>(vb1 + 16 * i) = z;
+    }
+    __syncthreads();
+  }
 
   // Persistent loop for the 8-wave instantiations (one workgroup per CU), as in
   // the forward's fast path; the 4-wave ones take one item per workgroup.
@@ -1030,8 +1058,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
   vec8 qb[KK], gb[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    qb[kk] = fold_vec(load_row8<T, true>(Qh, qrow, M, D, 16 * kk + 8 * h), qf);
-    gb[kk] = load_row8<T, true>(Gh, qrow, M, D, 16 * kk + 8 * h);
+    const bool in_d = !PAD || 16 * kk + 8 * h < D;  // padding chunks: zero
+    qb[kk] = fold_vec(load_row8<T, true>(Qh, in_d ? qrow : M, M, D, 16 * kk + 8 * h), qf);
+    gb[kk] = load_row8<T, true>(Gh, in_d ? qrow : M, M, D, 16 * kk + 8 * h);
   }
   float l2 = 0.0f, dl = 0.0f;
   if (qrow < M) {
@@ -1053,7 +1082,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
   static_assert(BSTEP % 16 == 0, "swizzle period");
   const int lds_w = __builtin_amdgcn_readfirstlane(w * 1024);
   auto issue = [&](const elt* src, int n0, char* buf) {
-    if (chunk >= L::CPR) return;  // D = 96: slots 12..15 of a row hold no data
+    if (chunk >= L::CPR) return;        // D = 96: slots 12..15 of a row hold no data
+    if (PAD && 8 * chunk >= D) return;  // padding: stays zero
     if (n0 + 64 <= N) {
       const char* base = reinterpret_cast<const char*>(src + (int64_t)n0 * D);
 #pragma unroll
@@ -1173,7 +1203,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_bwd_dq_fast_kernel(
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store_row4<T, true>(dQh, qrow, D, 32 * dt + 8 * g + 4 * h, dqa[dt], g, scale);
+        if (!PAD || 32 * dt + 8 * g + 4 * h < D)  // padding columns are not stored
+          store_row4<T, true>(dQh, qrow, D, 32 * dt + 8 * g + 4 * h, dqa[dt], g, scale);
   }
   }  // persistent loop
 }
@@ -1452,24 +1483,32 @@ struct BwdArgs {
   int dev;      // device of `stream`
 };
 
+// Smallest D of the padded fast path (at or below it the general kernels).
+constexpr int BWD_PAD_MIN_D = 32;
+
 template <class T, int DP, bool CAUSAL, bool DFULL>
 hipError_t launch_bwd_tiles(const BwdArgs& a) {
   using elt = typename T::elt;
   hipError_t e = hipSuccess;
+  // Fast kernels: D == DP, or (PAD) D a multiple of 8 above BWD_PAD_MIN_D,
+  // zero-padded to DP.
+  constexpr bool FAST_DP = DP == 64 || DP == 96 || DP == 128;
+  constexpr bool PAD = !DFULL;
+  const bool fast = FAST_DP && (DFULL || (a.D % 8 == 0 && a.D > BWD_PAD_MIN_D));
   if (a.N > 0) {
     const int ktiles = (a.N + BK - 1) / BK;
     bool done = false;
-    if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
-      if (a.M > 0) {
+    if constexpr (FAST_DP) {
+      if (fast && a.M > 0) {
         const int items = (int)(a.BH * ktiles);
         int slots = 0;  // the kernel loops over items at D >= 96 only
         if constexpr (DP >= 96)
-          slots = persistent_workgroups<fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>>(BT, a.dev);
+          slots = persistent_workgroups<fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF, PAD>>(BT, a.dev);
         const int P = slots >= NXCD && slots < items ? slots : items;
-        e = launch(fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF>, dim3((unsigned)P), dim3(BT),
+        e = launch(fa_bwd_dkdv_fast_kernel<T, DP, DKDV_NBUF, PAD>, dim3((unsigned)P), dim3(BT),
                    a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
                    (const elt*)a.dout, a.lse, (const float*)a.delta, (elt*)a.dk, (elt*)a.dv, a.M,
-                   a.N, ktiles, items, a.c, a.scale, CAUSAL ? 1 : 0, a.qf);
+                   a.N, ktiles, items, a.c, a.scale, CAUSAL ? 1 : 0, a.qf, a.D);
         done = true;
       }
     }
@@ -1481,19 +1520,19 @@ hipError_t launch_bwd_tiles(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (a.M > 0) {
-    if constexpr (DFULL && (DP == 64 || DP == 96 || DP == 128)) {
-      if (a.N > 0) {
+    if constexpr (FAST_DP) {
+      if (fast && a.N > 0) {
         constexpr int NW = DP == 64 ? 4 : 8;
         const int qtiles = (a.M + 32 * NW - 1) / (32 * NW);
         const int items = (int)(a.BH * qtiles);
         int slots = 0;  // the kernel loops over items with 8 waves only
         if constexpr (NW == 8)
-          slots = persistent_workgroups<fa_bwd_dq_fast_kernel<T, DP, NW>>(64 * NW, a.dev);
+          slots = persistent_workgroups<fa_bwd_dq_fast_kernel<T, DP, NW, PAD>>(64 * NW, a.dev);
         const int P = slots >= NXCD && slots < items ? slots : items;
-        return launch(fa_bwd_dq_fast_kernel<T, DP, NW>, dim3((unsigned)P), dim3(64 * NW),
+        return launch(fa_bwd_dq_fast_kernel<T, DP, NW, PAD>, dim3((unsigned)P), dim3(64 * NW),
                       a.stream, (const elt*)a.q, (const elt*)a.k, (const elt*)a.v,
                       (const elt*)a.dout, a.lse, (const float*)a.delta, (elt*)a.dq, a.M, a.N,
-                      qtiles, items, a.c, a.scale, CAUSAL ? 1 : 0, a.qf);
+                      qtiles, items, a.c, a.scale, CAUSAL ? 1 : 0, a.qf, a.D);
       }
     }
     const int qtiles = (a.M + BMQ - 1) / BMQ;

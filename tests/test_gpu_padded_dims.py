@@ -83,3 +83,57 @@ def test_padded_matches_general_kernel():
     assert not torch.isnan(o1).any() and not torch.isnan(o2).any()
     assert (o1.float() - o2.float()).abs().max().item() <= 2e-2
     assert np.abs((l1 - l2).cpu().numpy()).max() <= 2e-4
+
+
+def _run_bwd(w):
+    import torch
+
+    from gpu_calls import nan_bwd
+    from oracle.definition import scale_as_kernel
+    from parity_bwd import bounds, check as check_bwd
+    from workloads import make_dout
+
+    print(f"CASE bwd {w.name} B={w.B} H={w.H} M={w.M} N={w.N} D={w.D} {w.dtype} "
+          f"causal={w.causal}", flush=True)
+    qc, kc, vc = make_inputs(w)
+    gc = make_dout(w)
+    dev = torch.device("cuda:0")
+    q, k, v, g = qc.to(dev), kc.to(dev), vc.to(dev), gc.to(dev)
+    o, lse = nan_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = nan_bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    s = scale_as_kernel(w.scale)
+    flat = lambda x: x.reshape(-1, *x.shape[2:])
+    q64, k64, v64, g64 = (flat(x.double()).numpy() for x in (qc, kc, vc, gc))
+    o_gpu, l_gpu = flat(o.cpu().double()).numpy(), flat(lse.cpu().double()).numpy()
+    got = [flat(x.cpu().double()).numpy() for x in (dq, dk, dv)]
+    for hh in range(q64.shape[0]):
+        rq, rk, rv, parts = oracle.head_bwd(q64[hh], k64[hh], v64[hh], g64[hh], s, w.causal,
+                                            return_parts=True)
+        check(f"{w.name} head {hh} o", w.dtype, o_gpu[hh], l_gpu[hh], parts["O"], parts["lse"],
+              verbose=False)
+        bq, bk, bv = bounds(parts, q64[hh], k64[hh], g64[hh], s, w.dtype)
+        check_bwd(f"{w.name} head {hh} dq", w.dtype, got[0][hh], rq, bq, verbose=False)
+        check_bwd(f"{w.name} head {hh} dk", w.dtype, got[1][hh], rk, bk, verbose=False)
+        check_bwd(f"{w.name} head {hh} dv", w.dtype, got[2][hh], rv, bv, verbose=False)
+
+
+@pytest.mark.parametrize("D", PADDED_D)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_dims_backward(D, dtype, causal):
+    """The fast dK/dV and dQ kernels of the next size up with zero padding
+    chunks: 2 x 2 heads, ragged 64-row query and 128-row key tiles; causal with
+    M > N leaves rows with no key (their dQ is 0)."""
+    M, N = (270, 200) if causal else (200, 270)
+    _run_bwd(Workload(f"pad_bwd_{dtype}_D{D}_c{int(causal)}", 2, 2, M, N, D, dtype, causal,
+                      1 / math.sqrt(D), 500 + D))
+
+
+@pytest.mark.parametrize("D,dtype", [(112, "bf16"), (80, "f16")])
+def test_padded_dims_backward_persistent(D, dtype):
+    """More key tiles than CUs (4 x 32 heads x 3 tiles of 128 keys): the dK/dV
+    kernel at D above 64 loops over several items per workgroup; 300 queries
+    give the 8-wave dQ kernel two query tiles per head."""
+    _run_bwd(Workload(f"pad_bwd_persist_{dtype}_D{D}", 4, 32, 300, 300, D, dtype, True,
+                      1 / math.sqrt(D), 600 + D))
