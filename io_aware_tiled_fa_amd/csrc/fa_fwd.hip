@@ -1442,7 +1442,7 @@ hipError_t launch_lp_fast(const Launch& a) {
 }
 
 // Split-KV partials on the fast path (fp32 outputs into the workspace).
-template <class T, int DP, bool CAUSAL>
+template <class T, int DP, bool CAUSAL, bool PAD>
 hipError_t launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, float* opart,
                                 float* lpart) {
   using elt = typename T::elt;
@@ -1452,9 +1452,9 @@ hipError_t launch_lp_fast_split(const Launch& a, const KeySplit& ks, int G, floa
   const int qtiles = (a.M + rows - 1) / rows;
   const int items = (int)(a.BH * qtiles);  // one workgroup per item and chunk
   const dim3 grid((unsigned)items, (unsigned)G);
-  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, float, false>, grid, dim3(64 * NW), a.stream,
+  return launch(fa_fwd_lp_pipe_kernel<T, DP, NW, float, PAD>, grid, dim3(64 * NW), a.stream,
                 (const elt*)a.q, (const elt*)a.k, (const elt*)a.v, opart, lpart, a.M, a.N, off,
-                qtiles, items, a.c, ks, a.qf, DP);
+                qtiles, items, a.c, ks, a.qf, (int)a.D);
 }
 
 template <class T, bool CAUSAL>
@@ -1533,9 +1533,14 @@ hipError_t launch_f32_split(const Launch& a, const KeySplit& ks, int G, float* o
 }
 template <class T, bool CAUSAL>
 hipError_t dispatch_lp_split(const Launch& a, const KeySplit& ks, int G, float* op, float* lp) {
-  if (a.D == 128) return launch_lp_fast_split<T, 128, CAUSAL>(a, ks, G, op, lp);
-  if (a.D == 96) return launch_lp_fast_split<T, 96, CAUSAL>(a, ks, G, op, lp);
-  if (a.D == 64) return launch_lp_fast_split<T, 64, CAUSAL>(a, ks, G, op, lp);
+  if (a.D == 128) return launch_lp_fast_split<T, 128, CAUSAL, false>(a, ks, G, op, lp);
+  if (a.D == 96) return launch_lp_fast_split<T, 96, CAUSAL, false>(a, ks, G, op, lp);
+  if (a.D == 64) return launch_lp_fast_split<T, 64, CAUSAL, false>(a, ks, G, op, lp);
+  if (a.D % 8 == 0 && a.D > PAD_MIN_D) {  // zero-padded to the next fast size
+    if (a.D < 64) return launch_lp_fast_split<T, 64, CAUSAL, true>(a, ks, G, op, lp);
+    if (a.D < 96) return launch_lp_fast_split<T, 96, CAUSAL, true>(a, ks, G, op, lp);
+    return launch_lp_fast_split<T, 128, CAUSAL, true>(a, ks, G, op, lp);
+  }
   if (a.D <= 32) return launch_lp_split<T, 32, CAUSAL>(a, ks, G, op, lp);
   if (a.D <= 64) return launch_lp_split<T, 64, CAUSAL>(a, ks, G, op, lp);
   if (a.D <= 96) return launch_lp_split<T, 96, CAUSAL>(a, ks, G, op, lp);

@@ -22,14 +22,15 @@ pytestmark = pytest.mark.gpu
 PADDED_D = [40, 48, 56, 72, 80, 88, 104, 112, 120]
 
 
-def _run(w):
+def _run(w, splits=None):
     import torch
 
     print(f"CASE {w.name} B={w.B} H={w.H} M={w.M} N={w.N} D={w.D} {w.dtype} "
-          f"causal={w.causal} scale={w.scale:+.4f}", flush=True)
+          f"causal={w.causal} scale={w.scale:+.4f} splits={splits}", flush=True)
     qc, kc, vc = make_inputs(w)
     dev = torch.device("cuda:0")
-    o, lse = nan_fwd(qc.to(dev), kc.to(dev), vc.to(dev), causal=w.causal, scale=w.scale)
+    o, lse = nan_fwd(qc.to(dev), kc.to(dev), vc.to(dev), causal=w.causal, scale=w.scale,
+                     splits=splits)
     torch.cuda.synchronize()
     O_ref, L_ref = oracle.attention(qc.double().numpy(), kc.double().numpy(),
                                     vc.double().numpy(), w.scale, w.causal)
@@ -58,6 +59,15 @@ def test_padded_dims_persistent(D, dtype, causal):
     (D above 64) runs several items per workgroup; 200 keys, a ragged tail."""
     _run(Workload(f"pad_persist_{dtype}_D{D}_c{int(causal)}", 4, 32, 1000, 200, D, dtype, causal,
                   1 / math.sqrt(D), 400 + D))
+
+
+@pytest.mark.parametrize("D,dtype,causal,M,N,splits", [
+    (80, "bf16", True, 100, 3000, 3), (48, "f16", False, 1, 5000, 8), (120, "bf16", True, 16, 700, 5)])
+def test_padded_dims_split_kv(D, dtype, causal, M, N, splits):
+    """Split-KV on the padded path: the chunks' fp32 partials (rows of D
+    features in the workspace) and the LSE merge; decode-like shapes."""
+    _run(Workload(f"pad_split_{dtype}_D{D}_c{int(causal)}", 2, 4, M, N, D, dtype, causal,
+                  1 / math.sqrt(D), 700 + D), splits=splits)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.2])
