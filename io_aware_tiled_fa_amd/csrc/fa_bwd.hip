@@ -63,8 +63,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 //   positive scale of the score product (|scale|, or 1 for scale 0: fold_scale).
 // The fast dK/dV kernel loads them as the initial values of the dP and S
 // accumulators, so that the MFMAs leave dP - Delta and S - L / scale, and
-// P = exp2(c * acc) with c = scale * log2(e).  16 lanes per row.
-template <class T>
+// P = exp2(c * acc) with c = scale * log2(e).  LPR lanes per row (4 at
+// D <= 32, 8 at D <= 64, else 16), so that a row's 16-byte chunks keep every
+// lane busy.
+template <class T, int LPR>
 __global__ __launch_bounds__(BT) void fa_bwd_delta_kernel(const typename T::elt* __restrict__ o,
                                                           const typename T::elt* __restrict__ dout,
                                                           const float* __restrict__ lse,
@@ -72,27 +74,28 @@ __global__ __launch_bounds__(BT) void fa_bwd_delta_kernel(const typename T::elt*
                                                           int D, float scale) {
   using elt = typename T::elt;
   using vec8 = typename T::vec8;
-  const int sub = threadIdx.x >> 4;
-  const int l16 = threadIdx.x & 15;
-  for (int64_t row0 = (int64_t)blockIdx.x * 16; row0 < rows; row0 += (int64_t)gridDim.x * 16) {
+  constexpr int RPB = BT / LPR;  // rows per block and pass
+  const int sub = threadIdx.x / LPR;
+  const int l16 = threadIdx.x % LPR;
+  for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < rows; row0 += (int64_t)gridDim.x * RPB) {
     const int64_t row = row0 + sub;
     float acc = 0.0f;
     if (row < rows) {
       const elt* orow = o + row * D;
       const elt* grow = dout + row * D;
       if ((D & 7) == 0) {
-        for (int c8 = l16; 8 * c8 < D; c8 += 16) {
+        for (int c8 = l16; 8 * c8 < D; c8 += LPR) {
           const vec8 a = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(orow + 8 * c8));
           const vec8 b = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(grow + 8 * c8));
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
         }
       } else {
-        for (int d = l16; d < D; d += 16) acc = __builtin_fmaf((float)orow[d], (float)grow[d], acc);
+        for (int d = l16; d < D; d += LPR) acc = __builtin_fmaf((float)orow[d], (float)grow[d], acc);
       }
     }
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
     if (row < rows && l16 == 0) {
       ws[row] = -acc;
       const float x = lse[row];
@@ -1592,11 +1595,17 @@ template <class T, bool CAUSAL>
 hipError_t dispatch_bwd(const BwdArgs& a) {
   if (a.M > 0) {
     const int64_t rows = a.BH * a.M;
-    const int64_t blocks = (rows + 15) / 16;
-    const hipError_t e = launch(fa_bwd_delta_kernel<T>, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
-                                dim3(BT), a.stream, (const typename T::elt*)a.o,
-                                (const typename T::elt*)a.dout, a.lse, a.delta, rows, a.D,
-                                a.s_eff);
+    const int lpr = a.D <= 32 ? 4 : a.D <= 64 ? 8 : 16;
+    const int64_t blocks = (rows + BT / lpr - 1) / (BT / lpr);
+    const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+    using elt = typename T::elt;
+    const hipError_t e =
+        lpr == 4 ? launch(fa_bwd_delta_kernel<T, 4>, grid, dim3(BT), a.stream, (const elt*)a.o,
+                          (const elt*)a.dout, a.lse, a.delta, rows, a.D, a.s_eff)
+        : lpr == 8 ? launch(fa_bwd_delta_kernel<T, 8>, grid, dim3(BT), a.stream, (const elt*)a.o,
+                            (const elt*)a.dout, a.lse, a.delta, rows, a.D, a.s_eff)
+                   : launch(fa_bwd_delta_kernel<T, 16>, grid, dim3(BT), a.stream, (const elt*)a.o,
+                            (const elt*)a.dout, a.lse, a.delta, rows, a.D, a.s_eff);
     if (e != hipSuccess) return e;
   }
   if (a.D <= 32) return dispatch_full<T, 32, CAUSAL>(a);
