@@ -27,6 +27,10 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}"]
 C_FLAGS = ["-O2", "-fPIC", "-std=c11", "-Wall", "-Wextra", f"-I{INCLUDE}"]
+# The backward's kernels keep their MFMA accumulators in ordinary VGPRs where the
+# register budget allows (fewer v_accvgpr_read copies before the VALU uses S and
+# dP; measured 1-4 % faster, bit-identical).  The forward measured no gain.
+BWD_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:
@@ -57,7 +61,7 @@ def build(verbose: bool = False) -> str:
     bwd_o = os.path.join(BUILD, "fa_bwd.o")
     steps = [[cc, *C_FLAGS, "-c", os.path.join(CSRC, "fa_check.c"), "-o", check_o],
              [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_fwd.hip"), "-o", fwd_o],
-             [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "fa_bwd.hip"), "-o", bwd_o]]
+             [hipcc, *HIP_FLAGS, *BWD_FLAGS, "-c", os.path.join(CSRC, "fa_bwd.hip"), "-o", bwd_o]]
     with ThreadPoolExecutor(max_workers=len(steps)) as pool:  # independent translation units
         for f in [pool.submit(_run, cmd, verbose) for cmd in steps]:
             f.result()
