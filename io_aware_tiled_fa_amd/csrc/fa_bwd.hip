@@ -407,20 +407,7 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_kernel(
 // kernel owns every s_waitcnt vmcnt and barrier that orders a copy against its
 // readers.  M0 holds the LDS address of the copy (one wait state before the
 // load reads it) and is restored afterwards.  Lane l writes bytes
-// [16 l, 16 l + 16) (x4) or [4 l, 4 l + 4) (dword) after that address.
-__device__ __forceinline__ void lds_copy16(const void* g, unsigned lds_addr) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds_addr)
-      : "memory");
-}
-
+// [4 l, 4 l + 4) after that address (lds_copy_tile below: the 16-byte form).
 __device__ __forceinline__ void lds_copy4(const void* g, unsigned lds_addr) {
   unsigned saved;
   asm volatile(
