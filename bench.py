@@ -156,8 +156,9 @@ def cpu_baseline_bwd(w, qc, kc, vc, gc, budget_s: float = 15.0):
 def fwd_kernel_name(w, splits=0, cus=None):
     """The forward kernel(s) one fa_fwd (splits = 0) or fa_fwd_splitkv call
     launches for workload w, by the dispatch rules of fa_fwd.hip: fp16/bf16
-    with D in {64, 96, 128} run the pipelined direct-to-LDS kernel (split-KV
-    too), other 16-bit head dims the general kernel, fp32 the fp32 kernel (the
+    with D in {64, 96, 128}, or a multiple of 8 other than 32 (zero-padded to
+    the next of those), run the pipelined direct-to-LDS kernel (split-KV too),
+    other 16-bit head dims the general kernel, fp32 the fp32 kernel (the
     key-split one for small plain grids)."""
     if w.dtype == "f32":
         if splits:
@@ -170,7 +171,7 @@ def fwd_kernel_name(w, splits=0, cus=None):
             grid = w.B * w.H * ((w.M + 127) // 128)
             name = ("fa_fwd_f32_ksplit_kernel" if w.D <= 64 and w.N > 0 and 2 * grid < cus
                     else "fa_fwd_f32_kernel")
-    elif w.D in (64, 96, 128) and w.N > 0:
+    elif w.N > 0 and w.D % 8 == 0 and w.D != 32:
         name = "fa_fwd_lp_pipe_kernel"
     else:
         name = "fa_fwd_lp_kernel"

@@ -69,8 +69,9 @@ def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch)
 
 def test_kernel_label_follows_the_dispatch_rules():
     """roofline.kernel names what fa_fwd / fa_fwd_splitkv launch: the pipelined
-    kernel for 16-bit D in {64, 96, 128} (split-KV too), else the general or
-    fp32 kernels (the fp32 key-split kernel only for small plain grids)."""
+    kernel for 16-bit D in {64, 96, 128} and, zero-padded, the other multiples
+    of 8 except 32 (split-KV too), else the general or fp32 kernels (the fp32
+    key-split kernel only for small plain grids)."""
     sys.path.insert(0, ROOT)
     import bench
     from workloads import WORKLOADS
@@ -81,6 +82,10 @@ def test_kernel_label_follows_the_dispatch_rules():
     assert bench.fwd_kernel_name(w, splits=4) == pipe + " + fa_merge_kernel (split-KV)"
     for D in (64, 96):
         assert bench.fwd_kernel_name(w.with_(D=D), splits=2).startswith(pipe)
+    for D in (8, 40, 112):
+        assert bench.fwd_kernel_name(w.with_(D=D)) == pipe
+        assert bench.fwd_kernel_name(w.with_(D=D), splits=2).startswith(pipe)
+    assert bench.fwd_kernel_name(w.with_(D=32)) == "fa_fwd_lp_kernel"
     assert bench.fwd_kernel_name(w.with_(D=100)) == "fa_fwd_lp_kernel"
     assert bench.fwd_kernel_name(w.with_(D=100), splits=3).startswith("fa_fwd_lp_kernel +")
     f32 = WORKLOADS["single_head_f32"]
