@@ -575,16 +575,18 @@ __global__ __launch_bounds__(BT, 1) void fa_bwd_dkdv_fast_kernel(
     const unsigned dst = lds_w + (unsigned)(b * BUFB);
     // D = 96: slots 12..15 of a row hold no data; padding chunks stay zero
     if (chunk < L::CPR && (!PAD || 8 * chunk < D)) {
-      // Byte offsets within the head (M * D < 2^31 elements, so they fit 32 bits).
+      // Byte offsets within the head: M * D < 2^31 elements, so at two bytes
+      // each they fit 32 unsigned bits (formed in unsigned arithmetic).
+      const unsigned rowb = 2u * (unsigned)D;
       unsigned off[BPW];
-      const unsigned off0 = (unsigned)((q0 + cp_row) * D * 2 + 16 * chunk);
+      const unsigned off0 = (unsigned)(q0 + cp_row) * rowb + 16u * (unsigned)chunk;
       if (q0 + BQ <= M) {
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) off[i] = off0 + (unsigned)(i * BSTEP * D * 2);
+        for (int i = 0; i < BPW; ++i) off[i] = off0 + (unsigned)(i * BSTEP) * rowb;
       } else {
 #pragma unroll
         for (int i = 0; i < BPW; ++i)
-          off[i] = (unsigned)(min(q0 + cp_row + i * BSTEP, M - 1) * D * 2 + 16 * chunk);
+          off[i] = (unsigned)min(q0 + cp_row + i * BSTEP, M - 1) * rowb + 16u * (unsigned)chunk;
       }
       lds_copy_tile<BPW, NW * 1024, TB>(Qh, Gh, off, dst);
     }
