@@ -3,7 +3,9 @@ seeded sweep of random shapes: every dtype, head dims on and off the fast
 paths (1 to 128), M and N from one row to several tiles with ragged tails,
 M > N and M < N under the bottom-right causal mask, and positive, negative
 and zero scales.  The case list is drawn once from a fixed seed, so every run
-checks the same cases; each case's parameters are in its test id.  Outputs
+checks the same cases; each case's parameters are in its test id.  A second
+draw takes its head dims from the multiples of 8 that the 16-bit kernels
+zero-pad to the next fast size.  Outputs
 are prefilled with NaN (gpu_calls), so an element a kernel fails to write
 fails the comparison."""
 
@@ -22,14 +24,16 @@ from workloads import Workload, make_dout, make_inputs
 pytestmark = pytest.mark.gpu
 
 D_CHOICES = [1, 7, 16, 33, 40, 64, 64, 65, 96, 96, 100, 127, 128, 128]
+# Multiples of 8 that the 16-bit paths zero-pad to the next fast size.
+D_PADDED = [8, 24, 48, 56, 72, 80, 88, 104, 112, 120]
 
 
-def _cases(n: int, seed: int):
+def _cases(n: int, seed: int, d_choices=D_CHOICES, tag="r"):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         dtype = ("f32", "f16", "bf16")[i % 3]
-        D = int(rng.choice(D_CHOICES))
+        D = int(rng.choice(d_choices))
         M = int(rng.integers(1, 600))
         N = int(rng.integers(1, 800))
         B = int(rng.integers(1, 3))
@@ -43,15 +47,15 @@ def _cases(n: int, seed: int):
         else:
             scale = -float(rng.uniform(0.05, 0.5))
         splits = int(rng.choice([0, 0, 2, 5]))
-        name = (f"r{i}_{dtype}_B{B}H{H}_M{M}_N{N}_D{D}_{'causal' if causal else 'full'}"
+        name = (f"{tag}{i}_{dtype}_B{B}H{H}_M{M}_N{N}_D{D}_{'causal' if causal else 'full'}"
                 f"_s{scale:+.3f}_sp{splits}")
         out.append((Workload(name=name, B=B, H=H, M=M, N=N, D=D, dtype=dtype, causal=causal,
                              scale=scale, seed=7000 + i), splits))
     return out
 
 
-FWD_CASES = _cases(48, 20261203)
-BWD_CASES = [w for w, _ in _cases(24, 20261204)]
+FWD_CASES = _cases(48, 20261203) + _cases(24, 20261205, D_PADDED, "p")
+BWD_CASES = [w for w, _ in _cases(24, 20261204) + _cases(12, 20261206, D_PADDED, "p")]
 
 
 def _flat(x):
