@@ -89,9 +89,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * fa_fwd_general - the same operation, arguments, ownership and errors as
  * fa_fwd, always executed by the general kernel (K/V tiles staged through
  * registers, any D in 1..128) instead of the direct-to-LDS fast path fa_fwd
- * picks for fp16/bf16 with D in {64, 96, 128}.  Results agree with fa_fwd
- * within the accuracy stated for the dtype (the summation order is the same,
- * so they are usually bit-identical); it exists to cross-check the two paths.
+ * picks for fp16/bf16 with D in {64, 96, 128} (and, zero-padded to the next
+ * of those sizes, for the other multiples of 8 except 32).  Results agree
+ * with fa_fwd within the accuracy stated for the dtype (the summation order
+ * is the same, so they are usually bit-identical); it exists to cross-check
+ * the two paths.
  */
 int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
