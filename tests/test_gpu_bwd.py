@@ -197,15 +197,17 @@ def test_bwd_sum_rules_and_determinism():
     assert dk_sum.abs().max().item() <= 2e-2 * scale_dk + 1e-3
 
 
-def test_bwd_tensors_beyond_2_31_elements():
+@pytest.mark.parametrize("D,BH", [(128, 16385), (112, 18725)])
+def test_bwd_tensors_beyond_2_31_elements(D, BH):
     """Forward and backward with Q, K, V, dO and the gradients of more than 2^31
-    elements each (16385 heads of 1024 x 128, bf16, causal): every gradient of
-    the first head, the heads on either side of the 2^31-element offset and the
-    last head against the oracle.  Inputs are drawn on the GPU (seeded)."""
+    elements each (BH heads of 1024 x D, bf16, causal; D = 112 runs the fast
+    kernels zero-padded to 128): every gradient of the first head, the heads on
+    either side of the 2^31-element offset and the last head against the
+    oracle.  Inputs are drawn on the GPU (seeded)."""
     import torch
     from workloads import make_dout_device, make_inputs_device
 
-    w = _wl("bwd_big_bf16_causal", 1, 16385, 1024, 1024, 128, "bf16", True, 3201)
+    w = _wl(f"bwd_big_bf16_causal_d{D}", 1, BH, 1024, 1024, D, "bf16", True, 3201)
     per = w.M * w.D
     assert w.H * per > 2**31
     _say(f"{w} ({w.H * per} elements per tensor)")

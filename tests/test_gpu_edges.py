@@ -234,7 +234,8 @@ def test_fast_and_general_paths_agree(dtype, D, causal):
 @pytest.mark.parametrize("dtype,D,causal,BH", [
     ("bf16", 128, False, 16385),  # pipelined 16-bit kernel, 8 waves
     ("f16", 64, True, 32769),     # pipelined 16-bit kernel, 4 waves, causal
-    ("bf16", 100, False, 20972),  # general 16-bit kernel (D not a multiple of 32)
+    ("bf16", 100, False, 20972),  # general 16-bit kernel (D not a multiple of 8)
+    ("bf16", 112, True, 18725),   # pipelined kernel, zero-padded to 128
     ("f32", 32, True, 65537),     # fp32 kernel
 ])
 def test_tensors_beyond_2_31_elements(dtype, D, causal, BH):
